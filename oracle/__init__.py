@@ -1,0 +1,23 @@
+"""fp64 CPU oracle for weight-absorbed MLA decode.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link anything in this package: only the tests, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP library (no kernels, headers, helpers or constants) and imports
+nothing from ``decode_attention_absorbed_amd``.
+
+Every function here is pinned by the ``-m "not gpu"`` tests against
+something other than itself (brute force, closed forms, the unabsorbed
+multi-head form, scipy's softmax, invariants); none is "parity unpinned".
+"""
+from .mla_oracle import (  # noqa: F401
+    absorb_query,
+    attend_rows,
+    brute_force_ref,
+    gather_kv_rows,
+    lse_combine_ref,
+    mha_unabsorbed_ref,
+    mla_decode_ref,
+    mla_decode_split_ref,
+    visible_keys,
+)

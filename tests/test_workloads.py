@@ -1,0 +1,43 @@
+"""The seeded input generator: shapes and structure of the five workloads."""
+import numpy as np
+
+from workloads import CONFIGS, config_lens, make_inputs, pages_needed, to_bf16_bits, bf16_bits_to_f64
+
+
+def test_bf16_rounding_is_round_to_nearest_even():
+    # 1 + 2^-8 lies exactly between two bf16 values: ties go to the even mantissa (1.0)
+    x = np.array([1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -2.5, 0.0, np.inf, np.nan], dtype=np.float32)
+    bits = to_bf16_bits(x)
+    back = bf16_bits_to_f64(bits)
+    assert back[0] == 1.0
+    assert back[1] == 1.0 + 2.0**-6
+    assert back[2] == -2.5 and back[3] == 0.0 and np.isinf(back[4]) and np.isnan(back[5])
+
+
+def test_named_workload_structure():
+    lens = config_lens("mixed")
+    assert sorted(set(lens.tolist())) == [400, 20480]
+    assert (lens == 20480).sum() == 26 and (lens == 400).sum() == 38
+    assert sum(pages_needed(lens, 64)) == 8586
+    mtp = config_lens("mtp")
+    assert mtp.min() >= 1024 and mtp.max() <= 8192 and len(mtp) == 64
+    assert config_lens("long").tolist() == [131072]
+    assert config_lens("dsv3").tolist() == [4096] * 32
+    assert sorted(config_lens("tiny").tolist()) == [37, 100]
+
+
+def test_block_table_is_a_permutation_dealt_in_order():
+    x = make_inputs(5, 4, 1, 16, [17, 1, 64, 65, 100], seed=3, draw_values=False)
+    npg = pages_needed(x.seq_lens, 16)
+    seen = np.concatenate([x.block_table[b, :n] for b, n in enumerate(npg)])
+    assert sorted(seen.tolist()) == list(range(x.num_pages))
+    for b, n in enumerate(npg):
+        assert np.all(x.block_table[b, n:] == -1)
+
+
+def test_seeded_determinism():
+    a = make_inputs(2, 4, 2, 16, [20, 33], seed=9)
+    b = make_inputs(2, 4, 2, 16, [20, 33], seed=9)
+    for f in ("q_nope", "q_pe", "cache", "block_table", "seq_lens"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    assert set(CONFIGS) == {"tiny", "dsv3", "mtp", "mixed", "long"}

@@ -1,0 +1,235 @@
+"""Seeded synthetic inputs for absorbed-MLA decode.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the fp64 oracle (through the tests) and the HIP
+path (through the tests and the benchmark) take their inputs from here, so the
+two sides always see identical bits.
+
+Workload shapes come from the pages:
+
+* H = 128 heads, a 512-wide absorbed latent part and a 64-wide rope part per
+  query head, 576 bf16 values per cached token (Huawei, "DeepSeek V3/R1
+  inference deployment best practices on Ascend servers", section 7.2, the MLA
+  time model with its (576 + 512) x 128 terms; section 3.1.1 for the BF16
+  KV cache).
+* One MTP draft token, i.e. two query tokens per request (same report,
+  section 5.3 and the x2 factor in section 7.2).
+* A mixed batch of 20K-token (40%) and 400-token (60%) requests (Ascend
+  troubleshooting note on decode TPOT jitter, section 5.2, the random mixed
+  data set).
+
+Generation recipe (fixed draw order, ``numpy.random.default_rng(seed)``):
+  1. sequence lengths (only config "mtp" draws them),
+  2. a shuffle of the request order,
+  3. a permutation of all pages, dealt to the requests in order,
+  4. q_nope_absorbed, 5. q_pe, 6. the paged cache;
+values are float32 N(0, 1) rounded to bf16 (round-to-nearest-even).
+``num_pages`` is the exact number of pages the requests need; unused
+block-table entries hold -1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+D_QK = D_LATENT + D_ROPE  # 576
+
+#: The five named workloads.  ``lens`` is either a fixed list or a rule.
+CONFIGS: Dict[str, dict] = {
+    "tiny": dict(seed=1, batch=2, heads=16, q_len=1, page=16, lens=[37, 100]),
+    "dsv3": dict(seed=2, batch=32, heads=128, q_len=1, page=64, lens=[4096] * 32),
+    "mtp": dict(seed=3, batch=64, heads=128, q_len=2, page=64, lens=("uniform", 1024, 8192)),
+    # 40% of 64 = 25.6 requests, rounded to 26 long and 38 short.
+    "mixed": dict(seed=4, batch=64, heads=128, q_len=1, page=64, lens=[20480] * 26 + [400] * 38),
+    "long": dict(seed=5, batch=1, heads=128, q_len=1, page=64, lens=[131072]),
+}
+CONFIG_ORDER = ["tiny", "dsv3", "mtp", "mixed", "long"]
+
+
+def softmax_scale_default() -> float:
+    """1/sqrt(192) rounded to float32: the value the library receives.
+
+    192 = 128 (no-rope part) + 64 (rope part) is the per-head query/key width of
+    the unabsorbed attention; absorption changes the dot-product width to 576
+    but not the scale.
+    """
+    return float(np.float32(1.0 / np.sqrt(192.0)))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round-to-nearest-even) and return the raw uint16 bits.
+
+    NaN inputs stay NaN (a quiet NaN pattern).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounding = ((u >> 16) & 1) + 0x7FFF
+    r = ((u + rounding) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits to float64 exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+@dataclass
+class MLAInputs:
+    """One batch of decode inputs.  bf16 tensors are held as raw uint16 bits."""
+
+    name: str
+    batch: int
+    heads: int
+    q_len: int
+    page: int
+    seq_lens: np.ndarray  # int32 [B]
+    block_table: np.ndarray  # int32 [B, bt_stride], -1 padded
+    num_pages: int
+    q_nope: np.ndarray  # uint16 [B, q_len, H, 512]
+    q_pe: np.ndarray  # uint16 [B, q_len, H, 64]
+    cache: np.ndarray  # uint16 [num_pages, page, 576]
+    softmax_scale: float = field(default_factory=softmax_scale_default)
+
+    @property
+    def bt_stride(self) -> int:
+        return int(self.block_table.shape[1])
+
+    # float64 views for the oracle
+    def q_nope_f64(self) -> np.ndarray:
+        return bf16_bits_to_f64(self.q_nope)
+
+    def q_pe_f64(self) -> np.ndarray:
+        return bf16_bits_to_f64(self.q_pe)
+
+    def cache_f64(self) -> np.ndarray:
+        return bf16_bits_to_f64(self.cache)
+
+    def to_torch(self, device: str = "cpu") -> dict:
+        """Torch tensors (bf16 views of the same bits) for the HIP path."""
+        import torch
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+        return dict(
+            q_nope=bf16(self.q_nope),
+            q_pe=bf16(self.q_pe),
+            cache=bf16(self.cache),
+            block_table=torch.from_numpy(np.ascontiguousarray(self.block_table)).to(device),
+            seq_lens=torch.from_numpy(np.ascontiguousarray(self.seq_lens)).to(device),
+        )
+
+
+def pages_needed(lens: Sequence[int], page: int) -> List[int]:
+    return [-(-int(L) // page) for L in lens]
+
+
+def make_inputs(
+    batch: int,
+    heads: int,
+    q_len: int,
+    page: int,
+    lens: Sequence[int] | tuple,
+    seed: int,
+    name: str = "custom",
+    extra_pages: int = 0,
+    draw_values: bool = True,
+) -> MLAInputs:
+    """Draw one seeded batch following the fixed recipe in the module docstring.
+
+    ``lens`` is a list of per-request lengths or ``("uniform", lo, hi)`` for
+    integer lengths drawn uniformly from [lo, hi] (both ends included).
+    ``extra_pages`` appends unreferenced pages after the referenced ones (their
+    contents are drawn too, and callers may poison them).
+    """
+    rng = np.random.default_rng(seed)
+    if isinstance(lens, tuple) and lens and lens[0] == "uniform":
+        _, lo, hi = lens
+        base = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
+    else:
+        base = np.asarray(list(lens), dtype=np.int64)
+        if base.shape[0] != batch:
+            raise ValueError("len(lens) must equal batch")
+    order = rng.permutation(batch)
+    seq_lens = base[order].astype(np.int32)
+
+    npg = pages_needed(seq_lens, page)
+    used = int(sum(npg))
+    num_pages = used + int(extra_pages)
+    perm = rng.permutation(used).astype(np.int32)
+    bt_stride = max(1, max(npg) if npg else 1)
+    block_table = np.full((batch, bt_stride), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npg):
+        block_table[b, :n] = perm[off : off + n]
+        off += n
+
+    if draw_values:
+        q_nope = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_LATENT), dtype=np.float32))
+        q_pe = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_ROPE), dtype=np.float32))
+        cache = to_bf16_bits(rng.standard_normal((num_pages, page, D_QK), dtype=np.float32))
+    else:
+        q_nope = np.zeros((batch, q_len, heads, D_LATENT), np.uint16)
+        q_pe = np.zeros((batch, q_len, heads, D_ROPE), np.uint16)
+        cache = np.zeros((num_pages, page, D_QK), np.uint16)
+    return MLAInputs(
+        name=name,
+        batch=batch,
+        heads=heads,
+        q_len=q_len,
+        page=page,
+        seq_lens=seq_lens,
+        block_table=block_table,
+        num_pages=num_pages,
+        q_nope=q_nope,
+        q_pe=q_pe,
+        cache=cache,
+    )
+
+
+def make_config(name: str, seed: Optional[int] = None) -> MLAInputs:
+    """The named workload with its own seed (or an override)."""
+    c = CONFIGS[name]
+    return make_inputs(
+        batch=c["batch"],
+        heads=c["heads"],
+        q_len=c["q_len"],
+        page=c["page"],
+        lens=c["lens"],
+        seed=c["seed"] if seed is None else seed,
+        name=name,
+    )
+
+
+def config_lens(name: str) -> np.ndarray:
+    """Sequence lengths of a named workload without drawing the large tensors."""
+    c = CONFIGS[name]
+    x = make_inputs(c["batch"], c["heads"], c["q_len"], c["page"], c["lens"], c["seed"], name, draw_values=False)
+    return x.seq_lens
+
+
+def poison_tails(x: MLAInputs, value_bits: int = 0x7FC0) -> None:
+    """Fill the unused slots of every request's last page with NaN (in place)."""
+    for b in range(x.batch):
+        L = int(x.seq_lens[b])
+        n = -(-L // x.page)
+        tail = L - (n - 1) * x.page
+        if tail < x.page:
+            x.cache[x.block_table[b, n - 1], tail:, :] = value_bits
+
+
+def poison_unreferenced(x: MLAInputs, value_bits: int = 0x7FC0) -> None:
+    """Fill every page no request references with NaN (in place)."""
+    ref = np.zeros(x.num_pages, dtype=bool)
+    for b in range(x.batch):
+        n = -(-int(x.seq_lens[b]) // x.page)
+        ref[x.block_table[b, :n]] = True
+    x.cache[~ref] = value_bits
