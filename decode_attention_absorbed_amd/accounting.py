@@ -1,0 +1,61 @@
+"""Algorithmic FLOP and byte counts of absorbed-MLA decode, and MI355X peaks.
+
+FLOPs follow the convention of the Huawei Ascend report's MLA time model
+(section 7.2): each (query, head, key) pair costs 2 x 576 multiply-adds for
+QK^T and 2 x 512 for PV, i.e. 2 * (576 + 512) FLOPs.  The report counts every
+query against all L keys; by default this module counts only the keys a query
+may see (query j of a request with L keys sees L - q_len + 1 + j).
+
+Bytes are the compulsory HBM traffic: the cached rows of every request
+(576 bf16 each), the queries, the fp32 outputs and lse, the block table
+entries read and the sequence lengths.  Partials and re-reads are not counted,
+so they show up as a lower roofline fraction.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+D_QK, D_V = 576, 512
+ROW_BYTES = D_QK * 2  # bf16 row per cached token
+
+# MI355X published peaks (dense): HBM3E 8 TB/s, bf16 MFMA 2.5 PFLOP/s.
+PEAK_HBM_BYTES_PER_S = 8.0e12
+PEAK_BF16_FLOPS = 2.5e15
+
+
+def visible_key_count(seq_lens: Sequence[int], q_len: int) -> int:
+    return sum(q_len * (int(L) - q_len + 1) + q_len * (q_len - 1) // 2 for L in seq_lens)
+
+
+def flops(seq_lens: Sequence[int], heads: int, q_len: int, visible: bool = True) -> int:
+    keys = visible_key_count(seq_lens, q_len) if visible else q_len * sum(int(L) for L in seq_lens)
+    return 2 * (D_QK + D_V) * heads * keys
+
+
+def kv_bytes(seq_lens: Sequence[int]) -> int:
+    return ROW_BYTES * sum(int(L) for L in seq_lens)
+
+
+def algorithmic_bytes(seq_lens: Sequence[int], heads: int, q_len: int, page: int) -> int:
+    B = len(seq_lens)
+    rows = B * q_len * heads
+    q = rows * D_QK * 2
+    out = rows * D_V * 4 + rows * 4
+    bt = 4 * sum(-(-int(L) // page) for L in seq_lens) + 4 * B
+    return kv_bytes(seq_lens) + q + out + bt
+
+
+def roofline_seconds(seq_lens: Sequence[int], heads: int, q_len: int, page: int) -> dict:
+    """Time at the HBM and MFMA peaks and which one binds."""
+    f = flops(seq_lens, heads, q_len)
+    b = algorithmic_bytes(seq_lens, heads, q_len, page)
+    t_hbm = b / PEAK_HBM_BYTES_PER_S
+    t_mfma = f / PEAK_BF16_FLOPS
+    return {
+        "flops": f,
+        "bytes": b,
+        "t_hbm": t_hbm,
+        "t_mfma": t_mfma,
+        "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+        "t_bound": max(t_hbm, t_mfma),
+    }

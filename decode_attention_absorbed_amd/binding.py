@@ -1,0 +1,244 @@
+"""Thin ctypes binding over libmla_decode.so (argument marshalling only).
+
+Every step of the decode runs in the HIP library; this module checks torch
+tensors against the plan, passes raw device pointers and the current stream,
+and turns status codes into exceptions.  It never falls back to another
+implementation: if the library is missing, importing the symbols fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+# torch first: it loads the HIP runtime (libamdhip64.so.7) that the library
+# then shares, so device pointers and streams mean the same thing on both sides.
+import torch  # noqa: E402
+
+from .build import LIB_PATH
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+MLA_ERR_OUT_OF_MEMORY = 5
+
+MLA_Q_NUM_SEGMENTS = 0
+MLA_Q_NUM_WORKGROUPS = 1
+MLA_Q_NUM_PARTIALS = 2
+MLA_Q_ROWS_PER_BLOCK = 3
+MLA_Q_TILE_TOKENS = 4
+MLA_Q_NUM_ROW_BLOCKS = 5
+
+#: every symbol include/mla_decode.h declares
+EXPORTED = (
+    "mla_decode_plan",
+    "mla_decode_plan_host",
+    "mla_decode_workspace_bytes",
+    "mla_decode",
+    "mla_decode_plan_destroy",
+    "mla_status_string",
+    "mla_last_error",
+    "mla_plan_query",
+    "mla_plan_copy",
+)
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("MLA_DECODE_LIB", LIB_PATH)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raises loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m decode_attention_absorbed_amd.build`")
+    L = ctypes.CDLL(path)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vp = ctypes.c_void_p
+    L.mla_decode_plan.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
+    L.mla_decode_plan.restype = ctypes.c_int
+    L.mla_decode_plan_host.argtypes = L.mla_decode_plan.argtypes
+    L.mla_decode_plan_host.restype = ctypes.c_int
+    L.mla_decode_workspace_bytes.argtypes = [vp]
+    L.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_decode.argtypes = [
+        vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp,
+    ]
+    L.mla_decode.restype = ctypes.c_int
+    L.mla_decode_plan_destroy.argtypes = [vp]
+    L.mla_decode_plan_destroy.restype = None
+    L.mla_status_string.argtypes = [ctypes.c_int]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    L.mla_plan_query.argtypes = [vp, ctypes.c_int32]
+    L.mla_plan_query.restype = ctypes.c_int64
+    L.mla_plan_copy.argtypes = [vp, i32p, i32p]
+    L.mla_plan_copy.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != MLA_OK:
+        L = lib()
+        raise MLAError(status, f"{L.mla_status_string(status).decode()}: {L.mla_last_error().decode()}")
+
+
+class Plan:
+    """Owns an mla_plan*; destroyed with the object (or explicitly)."""
+
+    def __init__(self, handle: int, seq_lens: np.ndarray, q_len: int, num_heads: int, page_size: int, on_device: bool):
+        self.handle = handle
+        self.seq_lens = seq_lens
+        self.q_len = q_len
+        self.num_heads = num_heads
+        self.page_size = page_size
+        self.on_device = on_device
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def query(self, key: int) -> int:
+        return int(lib().mla_plan_query(self.handle, key))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(lib().mla_decode_workspace_bytes(self.handle))
+
+    def segments(self) -> np.ndarray:
+        """int32 [num_segments, 4]: request, first key, end key, partial id (-1 = whole)."""
+        n = self.query(MLA_Q_NUM_SEGMENTS)
+        seg = np.zeros((max(n, 1), 4), dtype=np.int32)
+        _check(lib().mla_plan_copy(self.handle, seg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None))
+        return seg[:n]
+
+    def workgroups(self) -> np.ndarray:
+        """int32 [grid, 4]: first segment, end segment, row block, 0."""
+        n = self.query(MLA_Q_NUM_WORKGROUPS)
+        wg = np.zeros((max(n, 1), 4), dtype=np.int32)
+        _check(lib().mla_plan_copy(self.handle, None, wg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return wg[:n]
+
+    def destroy(self) -> None:
+        if self.handle:
+            lib().mla_decode_plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def _make_plan(fn_name: str, seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int) -> Plan:
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    h = ctypes.c_void_p()
+    fn = getattr(lib(), fn_name)
+    _check(fn(lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(lens.shape[0]), int(q_len), int(num_heads), int(page_size), int(num_cus), ctypes.byref(h)))
+    return Plan(h.value, lens, q_len, num_heads, page_size, fn_name == "mla_decode_plan")
+
+
+def mla_decode_plan(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int = 0) -> Plan:
+    """Plan the split for one decode step (uploads the schedule to the current device)."""
+    return _make_plan("mla_decode_plan", seq_lens, q_len, num_heads, page_size, num_cus)
+
+
+def mla_decode_plan_host(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int) -> Plan:
+    """Host-only plan (no HIP call): for inspection and argument checks."""
+    return _make_plan("mla_decode_plan_host", seq_lens, q_len, num_heads, page_size, num_cus)
+
+
+def mla_decode_workspace_bytes(plan: Plan) -> int:
+    return plan.workspace_bytes
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+
+
+def mla_decode(
+    plan: Plan,
+    q_nope_absorbed: torch.Tensor,
+    q_pe: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    softmax_scale: float,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue the decode on `stream` (default: the current stream); returns (out, lse)."""
+    B, qlen, H = plan.batch, plan.q_len, plan.num_heads
+    dev = q_nope_absorbed.device
+    _expect(q_nope_absorbed, "q_nope_absorbed", torch.bfloat16, (B, qlen, H, 512))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, qlen, H, 64))
+    if kv_cache.dim() != 3 or kv_cache.shape[1] != plan.page_size or kv_cache.shape[2] != 576:
+        raise ValueError(f"kv_cache: shape {tuple(kv_cache.shape)}, expected [num_pages, {plan.page_size}, 576]")
+    _expect(kv_cache, "kv_cache", torch.bfloat16, tuple(kv_cache.shape))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table: shape {tuple(block_table.shape)}, expected [{B}, *]")
+    _expect(block_table, "block_table", torch.int32, tuple(block_table.shape))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, qlen, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, qlen, H), dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, (B, qlen, H, 512))
+    _expect(lse, "lse", torch.float32, (B, qlen, H))
+    need = plan.workspace_bytes
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(
+        lib().mla_decode(
+            plan.handle,
+            _ptr(q_nope_absorbed),
+            _ptr(q_pe),
+            _ptr(kv_cache),
+            int(kv_cache.shape[0]),
+            _ptr(block_table),
+            int(block_table.shape[1]),
+            _ptr(seq_lens),
+            float(softmax_scale),
+            _ptr(out),
+            _ptr(lse),
+            _ptr(workspace),
+            int(ws_bytes),
+            stream.cuda_stream,
+        )
+    )
+    return out, lse

@@ -1,0 +1,71 @@
+"""Builds libmla_decode.so (HIP kernels + C ABI + host planner) for gfx950, in-tree.
+
+    python -m decode_attention_absorbed_amd.build
+
+The library lands next to this file; the Python binding loads it from there.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmla_decode.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+SOURCES = ["mla_decode.hip", "plan.cpp"]
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # never emit packed fp32 math (v_pk_*_f32)
+    "-Xclang",
+    "-target-feature",
+    "-Xclang",
+    "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    if os.path.exists(cand):
+        return cand
+    found = shutil.which("hipcc")
+    if not found:
+        raise RuntimeError("hipcc not found (set ROCM_PATH)")
+    return found
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library; returns its path.  Always recompiles."""
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC]
+    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,174 @@
+/*
+ * mla_decode.h -- C ABI of libmla_decode.so: weight-absorbed MLA decode
+ * attention (DeepSeek-V3/R1 Multi-head Latent Attention) over a paged latent
+ * cache, flash-decoding style, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  Decode-time MLA in its weight-absorbed form, as
+ * the Huawei report "DeepSeek V3/R1 inference deployment best practices on
+ * Ascend servers" runs it (section 3.2.1: decode MLA with data parallelism and
+ * weight absorption; every head shares the compressed KV cache; section 6.1:
+ * a FlashAttention-style tiled attention operator; section 7.2: the
+ * (576 + 512) x 128-head work per key).  For request b, query token j and
+ * head h, with q = [q_nope_absorbed[b,j,h,0:512] | q_pe[b,j,h,0:64]] and the
+ * 576-wide cached row K_t of token t (V_t = its first 512 values):
+ *     n   = seq_lens[b] - q_len + 1 + j            (keys visible to query j)
+ *     s_t = softmax_scale * (q . K_t),  t < n
+ *     lse[b,j,h]    = ln sum_t exp(s_t)
+ *     out[b,j,h,:]  = sum_t exp(s_t - lse) * V_t
+ * The key range of each request is cut into pieces that run on different
+ * workgroups; the pieces are merged with a log-sum-exp combine (the
+ * flash-decoding split named in the Ascend troubleshooting note on decode TPOT
+ * jitter, section 4.2(3)).  How the range is cut is chosen by a planner that
+ * looks at all sequence lengths at once, so that a batch mixing long and short
+ * requests, or a single very long request, still fills every compute unit
+ * (the same note, section 5.1, names sequence-length-aware scheduling as the
+ * cure for the imbalance it diagnosed).
+ *
+ * Conventions
+ *  - bf16 = IEEE bfloat16 bits, fp32 = IEEE binary32.  All tensors are dense,
+ *    row-major (C order), with the shapes given below.
+ *  - "device" pointers point to memory of the current HIP device; "host"
+ *    pointers to ordinary host memory.  The caller owns every buffer it
+ *    passes; the library never frees or retains them beyond the call.
+ *  - Functions return an mla_status; none aborts, exits or throws.  On failure
+ *    mla_last_error() gives a human-readable detail (thread-local).
+ *  - Nothing here synchronizes the device.  Faults inside a kernel surface at
+ *    the caller's next synchronization.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,   /* a null pointer, a bad size, a plan/argument mismatch  */
+  MLA_ERR_UNSUPPORTED = 2,        /* a shape this build does not implement                  */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes < mla_decode_workspace_bytes(plan)     */
+  MLA_ERR_HIP = 4,                /* a HIP runtime call failed; detail in mla_last_error()  */
+  MLA_ERR_OUT_OF_MEMORY = 5       /* host or device allocation failed while planning        */
+} mla_status;
+
+/* Opaque split plan.  Immutable after creation; may be shared by any number of
+ * mla_decode calls (e.g. by every layer of one decode step), concurrently too,
+ * as long as concurrent calls use separate workspaces. */
+typedef struct mla_plan mla_plan;
+
+/*
+ * mla_decode_plan -- choose how the key ranges are split across workgroups.
+ *
+ *  seq_lens_host  host int32 [batch]: cached tokens of each request, counting
+ *                 the q_len new tokens (already written to the cache).  Each
+ *                 must satisfy q_len <= seq_lens_host[b] <= 2^24.
+ *  batch          >= 1.
+ *  q_len          query tokens per request, 1 <= q_len <= 8 (2 = one MTP draft
+ *                 token; query j sees one key more than query j-1).
+ *  num_heads      1 <= num_heads <= 128, and q_len * num_heads <= 1024.
+ *  page_size      tokens per cache page: a power of two, 16 <= page_size <= 4096.
+ *  num_cus        compute units to plan for; 0 = ask the current device.
+ *  plan_out       receives the new plan (set to NULL on failure).
+ *
+ * Allocates host memory and a small device buffer holding the schedule (it
+ * calls hipMalloc/hipMemcpy on the current device).  Release with
+ * mla_decode_plan_destroy.  Errors: MLA_ERR_INVALID_ARGUMENT,
+ * MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_MEMORY, MLA_ERR_HIP.
+ */
+mla_status mla_decode_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                           int32_t num_heads, int32_t page_size, int32_t num_cus,
+                           mla_plan** plan_out);
+
+/* Same as mla_decode_plan but makes no HIP call at all (num_cus must be > 0):
+ * the plan can be inspected with mla_plan_query but not run (mla_decode then
+ * returns MLA_ERR_INVALID_ARGUMENT).  For host-side tools and tests. */
+mla_status mla_decode_plan_host(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                                int32_t num_heads, int32_t page_size, int32_t num_cus,
+                                mla_plan** plan_out);
+
+/* Bytes of device workspace mla_decode needs with this plan (0 if no request
+ * is split).  The workspace holds one fp32 partial (rows x 512 values plus a
+ * log-sum-exp per row) per piece of every split request. */
+size_t mla_decode_workspace_bytes(const mla_plan* plan);
+
+/*
+ * mla_decode -- enqueue the decode attention for one layer on `stream`.
+ *
+ *  plan             from mla_decode_plan with the same seq_lens, q_len,
+ *                   num_heads and page_size.
+ *  q_nope_absorbed  device bf16 [B, q_len, H, 512]; 16-byte aligned.
+ *                   The query's no-rope part already multiplied by W_UK^T.
+ *  q_pe             device bf16 [B, q_len, H, 64]; 16-byte aligned; post-RoPE.
+ *  kv_cache         device bf16 [num_pages, page_size, 576]; 16-byte aligned.
+ *                   Row = [c_kv (512) | k_pe (64)]; V is the c_kv part.
+ *  num_pages        pages in kv_cache (> 0).  Page ids outside [0, num_pages)
+ *                   read page 0 instead of faulting (results are then garbage).
+ *  block_table      device int32 [B, bt_stride]: token t of request b lives in
+ *                   slot t % page_size of page block_table[b, t / page_size].
+ *                   Entries past ceil(seq_lens[b] / page_size) are never read;
+ *                   pages may be shared between requests (read only).
+ *  bt_stride        row stride of block_table, >= max_b ceil(seq_lens[b] / page_size).
+ *  seq_lens         device int32 [B]; must equal the lengths the plan was made
+ *                   with.  A request whose device length differs gets NaN in
+ *                   out and lse (loud, never an out-of-bounds access).
+ *  softmax_scale    finite, > 0 (1/sqrt(192) for DeepSeek-V3's 128 + 64 head dims).
+ *  out              device fp32 [B, q_len, H, 512], 16-byte aligned (normalized output).
+ *  lse              device fp32 [B, q_len, H]: natural log of the sum of exp of
+ *                   the scaled scores.
+ *  workspace        device buffer of >= mla_decode_workspace_bytes(plan) bytes,
+ *                   256-byte aligned (may be NULL when that size is 0).
+ *                   Contents on entry are ignored; it is scratch for this call.
+ *  stream           hipStream_t to enqueue on; NULL = the default stream.
+ *
+ * Enqueues at most two kernels, allocates nothing, never synchronizes.  The
+ * result is deterministic for a given plan.  Argument checks run on the host
+ * before any HIP call.  Errors: MLA_ERR_INVALID_ARGUMENT,
+ * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP (launch failure).
+ */
+mla_status mla_decode(const mla_plan* plan,
+                      const void* q_nope_absorbed, const void* q_pe,
+                      const void* kv_cache, int64_t num_pages,
+                      const int32_t* block_table, int32_t bt_stride,
+                      const int32_t* seq_lens, float softmax_scale,
+                      float* out, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Free a plan (its host memory and its device schedule).  NULL is a no-op.
+ * The plan must not be in use by a kernel still running. */
+void mla_decode_plan_destroy(mla_plan* plan);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status s);
+
+/* Detail of the last failure on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/*
+ * Plan inspection (host only; for tests and tools).
+ *  MLA_Q_NUM_SEGMENTS     number of (request, key range) pieces
+ *  MLA_Q_NUM_WORKGROUPS   grid size of the decode kernel
+ *  MLA_Q_NUM_PARTIALS     pieces that write a partial (0 when nothing is split)
+ *  MLA_Q_ROWS_PER_BLOCK   query rows (q_len*H flattened) one workgroup holds
+ *  MLA_Q_TILE_TOKENS      keys per tile
+ *  MLA_Q_NUM_ROW_BLOCKS   row blocks per request
+ * mla_plan_query returns the value (or -1 for an unknown key / NULL plan).
+ */
+enum { MLA_Q_NUM_SEGMENTS = 0, MLA_Q_NUM_WORKGROUPS = 1, MLA_Q_NUM_PARTIALS = 2,
+       MLA_Q_ROWS_PER_BLOCK = 3, MLA_Q_TILE_TOKENS = 4, MLA_Q_NUM_ROW_BLOCKS = 5 };
+int64_t mla_plan_query(const mla_plan* plan, int32_t key);
+
+/* Copy the pieces out: for segment i, seg[4*i + 0..3] = {request, first key,
+ * end key (exclusive), partial id or -1 when the piece is the whole request}.
+ * wg[4*w + 0..3] = {first segment, end segment, row block, 0} for workgroup w.
+ * Either pointer may be NULL.  Returns MLA_ERR_INVALID_ARGUMENT for a NULL plan. */
+mla_status mla_plan_copy(const mla_plan* plan, int32_t* seg, int32_t* wg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_absorbed_amd as mla
+from decode_attention_absorbed_amd import binding as bnd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mla_decode.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", src)))
+
+
+def test_header_declares_exactly_the_exported_symbols():
+    assert declared_functions() == sorted(bnd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mla.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = mla.lib()
+    for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_ARGUMENT"), (2, "MLA_ERR_UNSUPPORTED"),
+                       (3, "MLA_ERR_WORKSPACE_TOO_SMALL"), (4, "MLA_ERR_HIP"), (5, "MLA_ERR_OUT_OF_MEMORY")]:
+        assert L.mla_status_string(code).decode() == name
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=16, num_cus=8), 0),
+        (dict(seq_lens=[], q_len=1, num_heads=16, page_size=16, num_cus=8), 1),
+        (dict(seq_lens=[5], q_len=0, num_heads=16, page_size=16, num_cus=8), 1),
+        (dict(seq_lens=[5], q_len=9, num_heads=16, page_size=16, num_cus=8), 2),
+        (dict(seq_lens=[5], q_len=1, num_heads=0, page_size=16, num_cus=8), 1),
+        (dict(seq_lens=[5], q_len=1, num_heads=129, page_size=16, num_cus=8), 2),
+        (dict(seq_lens=[9], q_len=8, num_heads=128, page_size=16, num_cus=8), 0),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=8, num_cus=8), 2),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=48, num_cus=8), 2),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=8192, num_cus=8), 2),
+        (dict(seq_lens=[1], q_len=2, num_heads=16, page_size=16, num_cus=8), 1),
+        (dict(seq_lens=[5, 0], q_len=1, num_heads=16, page_size=16, num_cus=8), 1),
+        (dict(seq_lens=[(1 << 24) + 1], q_len=1, num_heads=16, page_size=16, num_cus=8), 2),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=16, num_cus=0), 1),
+    ],
+)
+def test_plan_argument_checks(args, status):
+    if status == 0:
+        p = mla.mla_decode_plan_host(**args)
+        assert p.handle
+        p.destroy()
+    else:
+        with pytest.raises(mla.MLAError) as e:
+            mla.mla_decode_plan_host(**args)
+        assert e.value.status == status
+        assert mla.lib().mla_last_error().decode() != ""
+
+
+def test_plan_out_null_and_query_null():
+    L = mla.lib()
+    lens = (ctypes.c_int32 * 1)(5)
+    assert L.mla_decode_plan_host(lens, 1, 1, 16, 16, 8, None) == 1
+    assert L.mla_plan_query(None, 0) == -1
+    assert L.mla_decode_workspace_bytes(None) == 0
+    assert L.mla_plan_copy(None, None, None) == 1
+    L.mla_decode_plan_destroy(None)  # no-op
+
+
+class _Fake:
+    """Non-null, suitably aligned fake device addresses (never dereferenced:
+    every check below fails on the host before any HIP call)."""
+
+    base = 1 << 40
+
+    def __init__(self):
+        self.n = 0
+
+    def __call__(self, align=256):
+        self.n += 1
+        return self.base + self.n * (1 << 20)
+
+
+def _call(plan, **over):
+    f = _Fake()
+    a = dict(
+        q=f(), qp=f(), cache=f(), num_pages=100, bt=f(), bt_stride=64, lens=f(), scale=1 / math.sqrt(192),
+        out=f(), lse=f(), ws=f(), ws_bytes=plan.workspace_bytes, stream=None,
+    )
+    a.update(over)
+    return mla.lib().mla_decode(
+        plan.handle, a["q"], a["qp"], a["cache"], a["num_pages"], a["bt"], a["bt_stride"], a["lens"], a["scale"],
+        a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"],
+    )
+
+
+@pytest.fixture(scope="module")
+def host_plan():
+    # one long request split over 64 slots -> the plan needs a workspace
+    p = mla.mla_decode_plan_host([4000, 17], 1, 128, 64, 64)
+    assert p.workspace_bytes > 0
+    yield p
+    p.destroy()
+
+
+def test_decode_rejects_null_pointers(host_plan):
+    for k in ("q", "qp", "cache", "bt", "lens", "out", "lse"):
+        assert _call(host_plan, **{k: None}) == 1, k
+
+
+def test_decode_rejects_misalignment(host_plan):
+    for k in ("q", "qp", "cache", "out"):
+        assert _call(host_plan, **{k: (1 << 40) + 8}) == 1, k
+    assert _call(host_plan, lse=(1 << 40) + 2) == 1
+    assert _call(host_plan, ws=(1 << 40) + 128) == 1
+
+
+def test_decode_rejects_bad_sizes(host_plan):
+    assert _call(host_plan, num_pages=0) == 1
+    assert _call(host_plan, bt_stride=62) == 1  # ceil(4000 / 64) = 63 pages needed
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert _call(host_plan, scale=s) == 1, s
+
+
+def test_decode_workspace_checks(host_plan):
+    assert _call(host_plan, ws_bytes=host_plan.workspace_bytes - 1) == 3
+    assert _call(host_plan, ws=None) == 1
+
+
+def test_decode_refuses_host_only_plan(host_plan):
+    assert _call(host_plan) == 1
+    assert "mla_decode_plan_host" in mla.lib().mla_last_error().decode()
+    assert _call(host_plan, bt_stride=63) == 1  # exactly enough pages is fine up to the plan check
+
+
+def test_plan_query_keys(host_plan):
+    assert host_plan.query(bnd.MLA_Q_ROWS_PER_BLOCK) in (64, 128)
+    assert host_plan.query(bnd.MLA_Q_TILE_TOKENS) in (32, 64)
+    assert host_plan.query(999) == -1
