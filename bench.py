@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of weight-absorbed MLA decode on one MI355X.
+
+One step = one layer's decode attention over one batch: the split-KV decode
+kernel and the log-sum-exp combine kernel, on a plan made once per decode step
+(the plan is reused by every layer; its host time is reported as plan_ms).
+Inputs are seeded synthetic bf16 tensors of the named workload, resident in HBM
+before timing starts.  To measure HBM rather than the 256 MB last-level cache,
+every step reads its own copy of the cache and queries (copies rotate, together
+larger than 1 GB).
+
+Prints ONE JSON line (value = algorithmic TFLOP/s of the whole step).
+
+    python bench.py [--config dsv3] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode attention TFLOP/s + HBM GB/s (% of roofline), H=128, 576-d latent"
+
+
+def kernel_sha() -> str:
+    """Hash of the kernel sources: counters taken for another build are stale."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "decode_attention_absorbed_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".cpp", ".h", ".inc")):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config: str, per_launch_bytes_alg: int):
+    """HBM bytes per decode launch measured with rocprofv3 counters (see
+    profiles/), or None if missing or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("decode_bytes_per_launch")
+
+
+def cpu_baseline(x, seconds: float) -> dict:
+    """The fp64 oracle on a bounded sample of requests of the same workload."""
+    import numpy as np
+
+    from decode_attention_absorbed_amd import accounting as acc
+    from oracle import mla_decode_ref
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cache = x.cache_f64()
+    qn, qp = x.q_nope_f64(), x.q_pe_f64()
+    done, flops, t0 = [], 0, time.perf_counter()
+    order = np.argsort(-x.seq_lens, kind="stable") if x.batch > 1 else np.arange(1)
+    for b in order:
+        mla_decode_ref(qn[b : b + 1], qp[b : b + 1], cache, x.block_table[b : b + 1], x.seq_lens[b : b + 1], x.softmax_scale)
+        done.append(int(b))
+        flops += acc.flops([int(x.seq_lens[b])], x.heads, x.q_len)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {x.batch} requests (fp64 numpy, {dt:.1f} s)",
+    }
+
+
+def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float) -> dict:
+    import torch
+
+    import decode_attention_absorbed_amd as mla
+    from decode_attention_absorbed_amd import accounting as acc
+    from decode_attention_absorbed_amd import binding as bnd
+    from workloads import CONFIGS, make_config
+
+    dev = torch.device("cuda:0")
+    x = make_config(config)
+    lens = [int(v) for v in x.seq_lens]
+    roof = acc.roofline_seconds(lens, x.heads, x.q_len, x.page)
+
+    t = x.to_torch(dev)
+    kv_bytes = t["cache"].numel() * 2
+    copies = max(1, min(16, -(-(1 << 30) // max(kv_bytes, 1))))
+    caches = [t["cache"]] + [t["cache"].clone() for _ in range(copies - 1)]
+    qns = [t["q_nope"]] + [t["q_nope"].clone() for _ in range(copies - 1)]
+    qps = [t["q_pe"]] + [t["q_pe"].clone() for _ in range(copies - 1)]
+    bt, sl = t["block_table"], t["seq_lens"]
+
+    tp0 = time.perf_counter()
+    plan = mla.mla_decode_plan(x.seq_lens, x.q_len, x.heads, x.page)
+    plan_ms = (time.perf_counter() - tp0) * 1e3
+    B, H, q = x.batch, x.heads, x.q_len
+    out = torch.empty((B, q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    L = mla.lib()
+    stream = torch.cuda.current_stream(dev)
+
+    def partials(i):
+        c = i % copies
+        bnd._check(
+            L.mla_decode_partials(
+                plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(), int(caches[c].shape[0]),
+                bt.data_ptr(), int(bt.shape[1]), sl.data_ptr(), float(x.softmax_scale), out.data_ptr(),
+                lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream,
+            )
+        )
+
+    def combine():
+        bnd._check(L.mla_decode_combine(plan.handle, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream))
+
+    for i in range(warmup):
+        partials(i)
+        combine()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        partials(i)
+        ev[i][1].record(stream)
+        combine()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    cmb_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    dec_avg = sum(dec_ms) / steps
+    cmb_avg = sum(cmb_ms) / steps
+
+    flops = roof["flops"]
+    nbytes = roof["bytes"]
+    bound = roof["bound"]
+    if bound == "hbm":
+        achieved = nbytes / (dec_avg * 1e-3) / 1e9
+        peak, unit = acc.PEAK_HBM_BYTES_PER_S / 1e9, "GB/s"
+    else:
+        achieved = flops / (dec_avg * 1e-3) / 1e12
+        peak, unit = acc.PEAK_BF16_FLOPS / 1e12, "TFLOP/s"
+    traffic = load_traffic(config, nbytes)
+    res = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, random page permutation)",
+        "config": {
+            "workload": config,
+            "batch": B,
+            "heads": H,
+            "q_len": q,
+            "page": x.page,
+            "seq_len": lens[0] if len(set(lens)) == 1 else f"{min(lens)}..{max(lens)}",
+            "kv_tokens": int(sum(lens)),
+        },
+        "hbm_gbps": nbytes / (ms_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": bound,
+            "achieved": achieved,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
+            "traffic": traffic,
+            "kernel": "decode_kernel",
+        },
+        "step_roofline_frac": roof["t_bound"] / (ms_step * 1e-3),
+        "decode_kernel_ms": dec_avg,
+        "decode_kernel_ms_p10_p90": [dec_ms[steps // 10], dec_ms[(9 * steps) // 10]],
+        "combine_kernel_ms": cmb_avg,
+        "plan_ms": plan_ms,
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "algorithmic_flops": flops,
+        "algorithmic_bytes": nbytes,
+        "input_copies": copies,
+        "num_workgroups": plan.query(bnd.MLA_Q_NUM_WORKGROUPS),
+        "num_partials": plan.query(bnd.MLA_Q_NUM_PARTIALS),
+        "kernel_sha": kernel_sha(),
+    }
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline(x, cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long")
+    ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by request; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.all:
+        for name in ["tiny", "dsv3", "mtp", "mixed", "long"]:
+            r = run(name, args.steps, args.warmup, False, 0.0)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+    res = run(args.config, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

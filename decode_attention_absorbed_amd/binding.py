@@ -39,6 +39,8 @@ EXPORTED = (
     "mla_decode_plan_host",
     "mla_decode_workspace_bytes",
     "mla_decode",
+    "mla_decode_partials",
+    "mla_decode_combine",
     "mla_decode_plan_destroy",
     "mla_status_string",
     "mla_last_error",
@@ -81,6 +83,10 @@ def lib() -> ctypes.CDLL:
         vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     L.mla_decode.restype = ctypes.c_int
+    L.mla_decode_partials.argtypes = L.mla_decode.argtypes
+    L.mla_decode_partials.restype = ctypes.c_int
+    L.mla_decode_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.mla_decode_combine.restype = ctypes.c_int
     L.mla_decode_plan_destroy.argtypes = [vp]
     L.mla_decode_plan_destroy.restype = None
     L.mla_status_string.argtypes = [ctypes.c_int]

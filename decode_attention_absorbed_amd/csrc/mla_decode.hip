@@ -98,11 +98,14 @@ __device__ __forceinline__ void wait_vmem_all() {
 // accumulator right before an MFMA reads it), and s_mfma_drain waits out the
 // XDL-write -> VALU-read latency (at most 18 wait states for a 16-pass MFMA)
 // before anything reads the results.
+// Like every MFMA issued as asm here it starts with s_nop 1: a VALU write of a
+// source register (e.g. a zeroed query row) needs two wait states before an
+// MFMA reads it, and the compiler adds none around inline asm.
 __device__ __forceinline__ void s_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
   if (first)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // The output accumulators O^T (16 tiles of 32x32 fp32 = 256 registers per
@@ -391,6 +394,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
           l_part += p;
           pb[i >> 3][i & 7] = (__bf16)p;
         }
+        // Materialize the bf16 operands here, not next to the MFMAs.
+        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- O^T += V^T P^T, V^T read transposed from the same block ----
@@ -457,10 +462,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
   auto slot_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
 
   float m = -INFINITY;
-  for (int s = 0; s < job.n; ++s) m = fmaxf(m, ws_lse[slot_of(s)]);
+  bool any_nan = false;  // fmaxf drops NaN; a NaN partial (length mismatch) must stay loud
+  for (int s = 0; s < job.n; ++s) {
+    const float v = ws_lse[slot_of(s)];
+    any_nan |= (v != v);
+    m = fmaxf(m, v);
+  }
   float lse_v = -INFINITY;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {
+  if (any_nan) {
+    lse_v = NAN;
+    acc = f32x4{NAN, NAN, NAN, NAN};
+  } else if (m != -INFINITY) {
     float z = 0.f;
     for (int s = 0; s < job.n; ++s) z += __expf(ws_lse[slot_of(s)] - m);
     lse_v = m + __logf(z);
@@ -471,9 +484,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
       const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + sl * 512 + c);
       acc += w * v;
     }
-  } else if (m != m) {  // NaN partials stay NaN
-    lse_v = m;
-    acc = f32x4{m, m, m, m};
   }
   *reinterpret_cast<f32x4*>(out + ((int64_t)job.b * rows + row) * 512 + c) = acc;
   if (c == 0) lse[(int64_t)job.b * rows + row] = lse_v;
@@ -578,6 +588,39 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Workspace checks shared by the entry points; splits it into the partial
+// outputs and the partial lse arrays.
+mla_status check_workspace(const mla_plan* plan, void* workspace, size_t workspace_bytes, float** ws_o,
+                           float** ws_lse) {
+  const mla::PlanData& d = plan->d;
+  const size_t need = mla::workspace_bytes(d);
+  *ws_o = nullptr;
+  *ws_lse = nullptr;
+  if (need == 0) return MLA_OK;
+  if (!workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL but the plan needs " + std::to_string(need) + " bytes");
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, the plan needs " + std::to_string(need));
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const size_t slots = (size_t)d.num_partials * d.nrb;
+  const size_t o_bytes = align256(slots * d.v.rows_per_block() * 512 * sizeof(float));
+  *ws_o = static_cast<float*>(workspace);
+  *ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  return MLA_OK;
+}
+
+// The plan's schedule lives on one device; refuse to run it from another.
+mla_status check_device(const mla_plan* plan) {
+  if (!plan->dev) return fail(MLA_ERR_INVALID_ARGUMENT, "plan was made by mla_decode_plan_host and cannot run");
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (device != plan->device)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "the current device is not the one the plan was made on");
+  return MLA_OK;
+}
+
 template <int NW, int TILE, bool SINGLE_PAGE>
 hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* cache,
                          int64_t num_pages, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
@@ -667,10 +710,10 @@ mla_status mla_plan_copy(const mla_plan* plan, int32_t* seg, int32_t* wg) {
   return MLA_OK;
 }
 
-mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe, const void* kv_cache,
-                      int64_t num_pages, const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                      float softmax_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
+                               const void* kv_cache, int64_t num_pages, const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, float softmax_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!q_nope_absorbed || !q_pe || !kv_cache || !block_table || !seq_lens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
@@ -686,32 +729,17 @@ mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const v
                                               std::to_string(d.max_pages) + ")");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-  const size_t need = mla::workspace_bytes(d);
-  if (need > 0) {
-    if (!workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL but the plan needs " + std::to_string(need) + " bytes");
-    if (workspace_bytes < need)
-      return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) +
-                                                   " bytes, the plan needs " + std::to_string(need));
-    if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  }
-  if (!plan->dev) return fail(MLA_ERR_INVALID_ARGUMENT, "plan was made by mla_decode_plan_host and cannot run");
-  int device = -1;
-  hipError_t e = hipGetDevice(&device);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (device != plan->device)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "the current device is not the one the plan was made on");
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws_o, &ws_lse);
+  if (st_ws != MLA_OK) return st_ws;
+  mla_status st_dev = check_device(plan);
+  if (st_dev != MLA_OK) return st_dev;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;
-  float* ws_o = nullptr;
-  float* ws_lse = nullptr;
-  if (need > 0) {
-    const size_t slots = (size_t)d.num_partials * d.nrb;
-    const size_t o_bytes = align256(slots * d.v.rows_per_block() * 512 * sizeof(float));
-    ws_o = static_cast<float*>(workspace);
-    ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-  }
   const bool single = d.page >= d.v.tile_tokens;
+  hipError_t e;
 #define MLA_LAUNCH(NW, TILE, SP)                                                                                 \
   launch_decode<NW, TILE, SP>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens, \
                               scale_log2, out, lse, ws_o, ws_lse, st)
@@ -723,16 +751,43 @@ mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const v
     return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
 #undef MLA_LAUNCH
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!out || !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (!aligned(out, 16) || !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws_o, &ws_lse);
+  if (st_ws != MLA_OK) return st_ws;
+  mla_status st_dev = check_device(plan);
+  if (st_dev != MLA_OK) return st_dev;
+  const mla::PlanData& d = plan->d;
   if (!d.jobs.empty()) {
     const char* base = static_cast<const char*>(plan->dev);
     hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)((d.rows + 1) / 2)), dim3(256),
-                       0, st, reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs), ws_o, ws_lse, d.rows,
+                       0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs), ws_o, ws_lse, d.rows,
                        d.v.rows_per_block(), d.nrb, out, lse);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   g_last_error.clear();
   return MLA_OK;
+}
+
+mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe, const void* kv_cache,
+                      int64_t num_pages, const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                      float softmax_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  mla_status s = mla_decode_partials(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
+                                     seq_lens, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+  if (s != MLA_OK) return s;
+  return mla_decode_combine(plan, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -137,6 +137,31 @@ mla_status mla_decode(const mla_plan* plan,
                       void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * The two halves of mla_decode, for callers that want to time, reorder or
+ * overlap them.  mla_decode == mla_decode_partials followed by
+ * mla_decode_combine on the same stream, with the same plan and workspace.
+ *
+ * mla_decode_partials -- the split decode kernel alone.  Same arguments and
+ *   checks as mla_decode.  Requests the plan keeps in one piece get their final
+ *   out/lse; pieces of split requests leave normalized partials in the workspace.
+ * mla_decode_combine -- merges the partials of split requests into out/lse
+ *   (the log-sum-exp combine).  A no-op kernel-wise when nothing is split.
+ *   out/lse as for mla_decode; the workspace must hold what the partials call
+ *   left there.  Errors: MLA_ERR_INVALID_ARGUMENT, MLA_ERR_WORKSPACE_TOO_SMALL,
+ *   MLA_ERR_HIP.
+ */
+mla_status mla_decode_partials(const mla_plan* plan,
+                               const void* q_nope_absorbed, const void* q_pe,
+                               const void* kv_cache, int64_t num_pages,
+                               const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, float softmax_scale,
+                               float* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Free a plan (its host memory and its device schedule).  NULL is a no-op.
  * The plan must not be in use by a kernel still running. */
 void mla_decode_plan_destroy(mla_plan* plan);

@@ -84,8 +84,12 @@ def test_forced_split_counts_agree(dev, num_cus):
     x = make_inputs(3, 128, 2, 64, [1500, 700, 90], seed=5)
     out, lse = run_gpu(x, dev, num_cus=num_cus)
     compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
+    # Different splits round P to bf16 against different running maxima, so the
+    # outputs agree to the bf16 level, not bitwise; the lse (fp32 sums) agrees closely.
     base_o, base_l = run_gpu(x, dev, num_cus=1)
-    assert np.max(np.abs(out - base_o)) < 1e-4 and np.max(np.abs(lse - base_l)) < 1e-4
+    assert np.max(np.abs(out - base_o)) < OUT_MAX_ABS
+    assert np.linalg.norm(out - base_o) / np.linalg.norm(base_o) < OUT_REL_L2
+    assert np.max(np.abs(lse - base_l)) < 1e-5
 
 
 # ---- the five named workloads at full size, oracle on sampled requests ------------------
@@ -176,10 +180,11 @@ def test_single_visible_key_returns_its_latent_row(dev):
         np.testing.assert_allclose(lse[b, 0], s, rtol=0, atol=1e-3)
 
 
-def test_device_length_mismatch_is_loud(dev):
-    x = make_inputs(2, 16, 1, 16, [40, 70], seed=15)
-    wrong = torch.tensor([40, 69], dtype=torch.int32, device=dev)
-    out, lse = run_gpu(x, dev, seq_lens_dev=wrong)
+@pytest.mark.parametrize("num_cus", [1, 256])  # request 1 whole, and split (NaN through the combine)
+def test_device_length_mismatch_is_loud(dev, num_cus):
+    x = make_inputs(2, 16, 1, 16, [40, 170], seed=15)
+    wrong = torch.tensor([40, 169], dtype=torch.int32, device=dev)
+    out, lse = run_gpu(x, dev, num_cus=num_cus, seq_lens_dev=wrong)
     assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
 
 
