@@ -7,16 +7,20 @@
 // the heads as the M dimension, QK^T and PV are dense contractions against a
 // shared key tile, so both run on bf16 MFMA with fp32 accumulation.
 //
-// Decode kernel, one workgroup = NW waves = 32*NW query rows (rows are the
+// Decode kernel: one workgroup = 4 waves = 128 query rows (rows are the
 // flattened (query token, head) pairs of one request), walking one or more
-// pieces of key range:
-//  * a tile of TILE keys x 576 bf16 is copied HBM -> LDS with 16-byte direct
-//    loads (global_load_lds_dwordx4), double buffered, one barrier per tile.
-//    Rows are stored with a 16-byte pad (1168 B stride) so that both the
-//    row-wise reads of QK^T and the transposed reads of PV hit distinct banks;
+// pieces of key range in tiles of 32 keys:
+//  * tiles are copied HBM -> LDS with 16-byte direct loads
+//    (global_load_lds_dwordx4) into a ring of NSTAGE buffers; while tile i is
+//    computed, tiles i+1 .. i+NSTAGE-1 are in flight (about 110 KB per CU, to
+//    cover HBM latency at full bandwidth).  One barrier per tile;
+//  * a cached row is 72 chunks of 16 bytes; inside each aligned group of 8
+//    chunks, chunk c of key row t is stored at c ^ swz(t).  The swizzle makes
+//    both the row reads of QK^T (16 rows, same chunk) and the transposed reads
+//    of PV (4 rows x 4 chunks) hit 16 distinct 4-bank groups;
 //  * wave w keeps its 32 query rows, as the B operand of
 //    v_mfma_f32_32x32x16_bf16, in 144 VGPRs for the whole piece, and computes
-//    S^T = K Q^T for 32 keys at a time (A operand = key rows read from LDS);
+//    S^T = K Q^T for the tile's 32 keys (A operand = key rows read from LDS);
 //    in that layout each lane holds one head and 16 keys, so the row maximum
 //    needs one cross-half swap and the running (max, sum) is lane-local;
 //  * online softmax in base 2 with a lazy reference: the output is rescaled
@@ -51,25 +55,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kRowBytesHbm = 576 * 2;  // one cached token
-constexpr int kChunksHbm = 72;         // 16-byte chunks per cached token
-constexpr int kChunksLds = 73;         // plus one pad chunk in LDS
-constexpr int kRowBytesLds = kChunksLds * 16;
+constexpr int kRowBytes = 576 * 2;  // one cached token (HBM and LDS)
+constexpr int kChunks = 72;         // 16-byte chunks per cached token
+constexpr int kTile = 32;           // keys per tile
+constexpr int kWaves = 4;
+constexpr int kRowsPerBlock = 32 * kWaves;
+constexpr int kStageBytes = kTile * kRowBytes;         // 36864
+constexpr int kLoadsPerTile = kTile * kChunks / 64;     // 36 one-KB copies
+constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;  // 9
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of copies");
 
-template <int NW, int TILE>
-struct Shape {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kRowsPerBlock = 32 * NW;
-  static constexpr int kBlocks = TILE / 32;            // 32-key MFMA blocks per tile
-  static constexpr int kKSteps = TILE / 16;            // 16-key PV steps per tile
-  static constexpr int kPositions = TILE * kChunksLds; // 16-byte LDS slots per tile
-  static constexpr int kLoads = (kPositions + 63) / 64;
-  static constexpr int kLoadsPerWave = (kLoads + NW - 1) / NW;
-  static constexpr int kBufBytes = kLoads * 1024;
-  static_assert(TILE == 32 || TILE == 64, "tile is 32 or 64 keys");
-};
+// Chunk swizzle of key row t (t = row within the tile).
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 
 __device__ __forceinline__ float partner_max(float x) {
   // permlane32_swap(x, x) returns {lanes 0-31: x, 32-63: x of lane-32} and
@@ -83,11 +82,40 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void wait_vmem_all() {
-  // s_waitcnt vmcnt(0) (expcnt, lgkmcnt at their maxima).  It also covers the
-  // LDS copies issued as inline asm; issued as the builtin so that the
-  // compiler's own wait-count bookkeeping sees that every load has landed.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (N is an immediate).  The query loads and LDS copies are inline asm the
+// compiler does not count, so every wait on them is explicit.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte global -> LDS copies (global_load_lds_dwordx4).  Each lane names its
+// own source; the 64 lanes of the wave fill 1 KB of LDS starting at M0.  They
+// are issued as inline asm on purpose: the compiler's wait-count pass treats a
+// pending LDS copy as aliasing every later LDS read and would insert
+// s_waitcnt vmcnt(0) before them, serializing the copy of later tiles with the
+// compute on this one.  (s_nop 0: one wait state between the M0 write and the
+// copy that reads it.)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
+}
+
+__device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, uint32_t lds_dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_dst) : "memory");
+}
+
+// 16-byte global load into VGPRs, invisible to the compiler's wait counts
+// (the explicit wait before the first QK^T covers it).
+__device__ __forceinline__ bf16x8 load16(const void* src) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+  return v;
 }
 
 // The S^T accumulators are pinned to VGPRs (the softmax reads them with VALU
@@ -96,17 +124,17 @@ __device__ __forceinline__ void wait_vmem_all() {
 // asm with a VGPR constraint.  The hazards the compiler cannot see inside the
 // asm are handled here: the first step takes srcC = 0 (no VALU write of the
 // accumulator right before an MFMA reads it), and s_mfma_drain waits out the
-// XDL-write -> VALU-read latency (at most 18 wait states for a 16-pass MFMA)
-// before anything reads the results.
-// Like every MFMA issued as asm here it starts with s_nop 1: a VALU write of a
-// source register (e.g. a zeroed query row) needs two wait states before an
-// MFMA reads it, and the compiler adds none around inline asm.
+// XDL-write -> VALU-read latency before anything reads the results.  Every
+// MFMA issued as asm starts with s_nop 1: a VALU write of a source register
+// needs two wait states before an MFMA reads it.
 __device__ __forceinline__ void s_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
   if (first)
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
   else
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+
+__device__ __forceinline__ void s_mfma_drain(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc)); }
 
 // The output accumulators O^T (16 tiles of 32x32 fp32 = 256 registers per
 // lane) live in the physical AGPRs a[0:255]: tile cb is a[16cb : 16cb+15].
@@ -116,8 +144,7 @@ __device__ __forceinline__ void s_mfma(f32x16& acc, const bf16x8& a, const bf16x
 // Hazards the compiler cannot see are handled where the code runs:
 //  * MFMA -> accvgpr_read of the results: o_drain waits 24 wait states;
 //  * accvgpr_write (rescale) -> MFMA srcC: the whole softmax runs in between,
-//    plus an s_nop at the head of the PV loop;
-//  * VALU-written P operand -> MFMA srcA/B: same s_nop.
+//    plus the s_nop in front of every MFMA.
 template <int CB>
 struct OTile;
 template <int N>
@@ -128,12 +155,12 @@ __device__ __forceinline__ void o_set(float x);
 
 // Dispatch on a tile index that is a constant after unrolling.
 __device__ __forceinline__ void o_mfma(int cb, const bf16x8& a, const bf16x8& b, bool first) {
-#define MLA_CASE(n)                 \
-  case n:                           \
-    if (first)                      \
-      OTile<n>::mfma_first(a, b);   \
-    else                            \
-      OTile<n>::mfma(a, b);         \
+#define MLA_CASE(n)               \
+  case n:                         \
+    if (first)                    \
+      OTile<n>::mfma_first(a, b); \
+    else                          \
+      OTile<n>::mfma(a, b);       \
     break;
   switch (cb) {
     MLA_CASE(0) MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7)
@@ -175,38 +202,16 @@ __device__ __forceinline__ void o_store_rec(float* dst, int half, float inv) {
   }
 }
 
-__device__ __forceinline__ void s_mfma_drain(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc)); }
-
-// 16-byte global -> LDS copies (global_load_lds_dwordx4).  Each lane names its
-// own source; the 64 lanes of the wave fill 1 KB of LDS starting at M0.  They
-// are issued as inline asm on purpose: the compiler's wait-count pass treats a
-// pending LDS-DMA as aliasing every later LDS read and would insert
-// s_waitcnt vmcnt(0) before them, serializing the copy of tile i+1 with the
-// compute on tile i.  Completion is awaited explicitly (wait_vmem_all) before
-// the barrier that publishes a tile.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// (s_nop 0: one wait state between the M0 write and the LDS-DMA that reads it.)
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst));
-}
-
-__device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_dst));
-}
-
-// Page ids a tile touches (uniform; at most 4 since pages hold >= 16 keys and
-// tiles <= 64).  Out-of-range ids are replaced by page 0 so that a corrupt
+// Page ids a tile touches (uniform; at most 2 since pages hold >= 16 keys and
+// tiles hold 32).  Out-of-range ids are replaced by page 0 so that a corrupt
 // block table can never make the kernel read outside the cache.
 struct TilePages {
   int first;
-  int pg[4];
+  int pg[2];
 };
 
-template <int NW, int TILE, bool SINGLE_PAGE>
-__global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
+template <int NSTAGE, bool SINGLE_PAGE>
+__global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint8_t* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ block_table, int32_t bt_stride,
@@ -215,8 +220,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_lse) {
-  using S = Shape<NW, TILE>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * S::kBufBytes];
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2..4 LDS stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * kStageBytes];
 
   const WorkgroupRange wr = wgs[blockIdx.x];
   if (wr.seg_begin >= wr.seg_end) return;
@@ -226,19 +231,39 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
   const int half = lane >> 5;  // which 8-wide k slice of an MFMA operand this lane holds
   const int rb = wr.row_block;
   const int row_local = wave * 32 + (lane & 31);
-  const int row = rb * S::kRowsPerBlock + row_local;
+  const int row = rb * kRowsPerBlock + row_local;
   const bool row_ok = row < rows;
   const int jq = row_ok ? row / heads : 0;  // query token of this row
   const int psize = 1 << page_log2;
 
-  // Per-lane LDS byte offsets (within a buffer) of the operand reads.
-  // QK^T, A operand = key rows: key (lane & 31) of the 32-key block, k slice `half`.
-  const int qk_off = (lane & 31) * kRowBytesLds + half * 16;
+  // Per-lane LDS byte offsets (within a stage) of the operand reads.
+  // QK^T, A operand = key rows: key t = lane & 31, logical chunk 2*kk + half,
+  // stored at chunk (2*kk + half) ^ swz(t) of its 8-group.  For kk = 4*g + m
+  // the offset is qk_base[m] + 128*g.
+  int qk_base[4];
+  {
+    const int t = lane & 31;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qk_base[m] = t * kRowBytes + 16 * ((2 * m + half) ^ swz(t));
+  }
   // PV, A operand = V^T via transposed reads: within each 16-lane group g, lane k
   // addresses key row (k / 4) of a 4-key strip, columns 4 * (k % 4) .. + 3 of a
-  // 16-column strip; the read hands lane k column k of the 4 x 16 block.
-  const int grp = lane >> 4, k16 = lane & 15;
-  const int pv_off = (4 * half + (k16 >> 2)) * kRowBytesLds + (16 * (grp & 1) + 4 * (k16 & 3)) * 2;
+  // 16-column strip; the read hands lane k column k of the 4 x 16 block.  Key
+  // row r = 16*ks + 8*qq + 4*half + k/4, column 32*cb + 16*(g&1) + 4*(k&3); its
+  // chunk (column / 8) is swizzled by the row.  The offset is
+  // pv_base[qq][cb&1] + 18432*ks + 128*(cb>>1).
+  int pv_base[2][2];
+  {
+    const int grp = lane >> 4, k16 = lane & 15;
+    const int clow = 2 * (grp & 1) + ((k16 & 3) >> 1);  // chunk within a 4-chunk (32-column) group
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int r = 8 * qq + 4 * half + (k16 >> 2);
+#pragma unroll
+      for (int odd = 0; odd < 2; ++odd)
+        pv_base[qq][odd] = r * kRowBytes + 16 * ((4 * odd + clow) ^ swz(r)) + 8 * (k16 & 1);
+    }
+  }
 
   for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
     const Segment sg = segs[si];
@@ -250,176 +275,228 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     // Keys this row may see inside the piece: [kv0, lim).
     const int lim = row_ok ? min(kv1, L - q_len + 1 + jq) : kv0;
 
-    // Block-table entries of a tile: loaded one tile ahead of use (scalar
-    // loads), checked against num_pages when used.
+    // Block-table entries of a tile (scalar loads, checked when used).
     auto fetch_pages = [&](int tb) {
       TilePages tp;
       tp.first = tb >> page_log2;
-      const int last = (min(tb + TILE, kv1) - 1) >> page_log2;
-#pragma unroll
-      for (int k = 0; k < (SINGLE_PAGE ? 1 : 4); ++k) tp.pg[k] = bt_row[min(tp.first + k, last)];
-      if (SINGLE_PAGE) tp.pg[1] = tp.pg[2] = tp.pg[3] = tp.pg[0];
+      const int last = (min(tb + kTile, kv1) - 1) >> page_log2;
+      tp.pg[0] = bt_row[tp.first];
+      tp.pg[1] = SINGLE_PAGE ? tp.pg[0] : bt_row[min(tp.first + 1, last)];
       return tp;
     };
     auto checked = [&](TilePages tp) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) tp.pg[k] = ((uint64_t)(int64_t)tp.pg[k] < (uint64_t)num_pages) ? tp.pg[k] : 0;
+      for (int k = 0; k < 2; ++k) tp.pg[k] = ((uint64_t)(int64_t)tp.pg[k] < (uint64_t)num_pages) ? tp.pg[k] : 0;
       return tp;
     };
 
-    // One 1 KB direct-to-LDS copy: LDS slots [64 n, 64 n + 64) of the tile,
-    // slot = 73 * key + chunk (chunk 72 is the row pad and is not loaded).
-    auto dma = [&](int i, int tb, const TilePages& tp, uint8_t* lbase) {
-      const int n = i * NW + wave;
-      if (n < S::kLoads) {
-        int lane_v = lane;
-        asm volatile("" : "+v"(lane_v));  // keep the address math next to its use
-        const int pos = n * 64 + lane_v;
-        const int t = pos / kChunksLds;
-        const int c = pos - t * kChunksLds;
-        if (c < kChunksHbm && t < TILE) {
-          const int tok = min(tb + t, kv1 - 1);
-          const uint32_t lds_dst = lds_addr(lbase + n * 1024);
-          if (SINGLE_PAGE) {
-            const uint8_t* pbase = cache + ((int64_t)tp.pg[0] << page_log2) * kRowBytesHbm;
-            const uint32_t off = (uint32_t)((tok & (psize - 1)) * kRowBytesHbm + c * 16);
-            dma16_saddr(pbase, off, lds_dst);
-          } else {
-            const int k = (tok >> page_log2) - tp.first;
-            const int page = k == 0 ? tp.pg[0] : (k == 1 ? tp.pg[1] : (k == 2 ? tp.pg[2] : tp.pg[3]));
-            dma16(cache + (((int64_t)page << page_log2) + (tok & (psize - 1))) * kRowBytesHbm + c * 16, lds_dst);
-          }
-        }
+    // Copy i of this wave for the tile at key tb: LDS slots [64 n, 64 n + 64)
+    // of the stage, n = i * 4 + wave; slot p holds chunk (p % 72) ^ swz of key
+    // p / 72.  Keys past the piece are clamped to its last key (their scores
+    // are masked; the copy stays inside the request's pages).
+    auto dma = [&](int i, int tb, const TilePages& tp, uint8_t* stage) {
+      const int n = i * kWaves + wave;
+      int lane_v = lane;
+      asm volatile("" : "+v"(lane_v));  // keep the address math next to its use
+      const int pos = n * 64 + lane_v;
+      const int t = pos / kChunks;
+      const int pc = pos - t * kChunks;
+      const int c = pc ^ swz(t);
+      const int tok = min(tb + t, kv1 - 1);
+      const uint32_t lds_dst = lds_addr(stage + n * 1024);
+      if (SINGLE_PAGE) {
+        const uint8_t* pbase = cache + ((int64_t)tp.pg[0] << page_log2) * kRowBytes;
+        dma16_saddr(pbase, (uint32_t)((tok & (psize - 1)) * kRowBytes + c * 16), lds_dst);
+      } else {
+        const int page = ((tok >> page_log2) == tp.first) ? tp.pg[0] : tp.pg[1];
+        dma16(cache + (((int64_t)page << page_log2) + (tok & (psize - 1))) * kRowBytes + c * 16, lds_dst);
       }
     };
 
-    // All waves must be done with the previous piece's last tile before the
-    // first tile of this one lands in LDS.
+    const int ntiles = (kv1 - kv0 + kTile - 1) / kTile;
+
+    // All waves must be done with the previous piece's tiles before the first
+    // tiles of this one land in LDS.
     __syncthreads();
 
-    const int ntiles = (kv1 - kv0 + TILE - 1) / TILE;
-    TilePages pg_next = checked(fetch_pages(kv0));
-#pragma unroll
-    for (int i = 0; i < S::kLoadsPerWave; ++i) dma(i, kv0, pg_next, smem);
-    TilePages pg_raw = pg_next;
-    if (ntiles > 1) pg_raw = fetch_pages(kv0 + TILE);
-
     // Query rows as the MFMA B operand: lane holds dims 16*kk + 8*half .. +7.
+    // Issued first so that the wait for tile 0 also covers them.
     bf16x8 q[36];
-    if (row_ok) {
-      const bf16x8* qn = reinterpret_cast<const bf16x8*>(q_nope + ((int64_t)b * rows + row) * 512);
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_pe + ((int64_t)b * rows + row) * 64);
+    {
+      const int qrow = row_ok ? row : 0;  // rows past the end load row 0 and are zeroed below
+      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * half;
+      const uint16_t* qp = q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * half;
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) q[kk] = qn[2 * kk + half];
+      for (int kk = 0; kk < 32; ++kk) q[kk] = load16(qn + 16 * kk);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[32 + kk] = qp[2 * kk + half];
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 36; ++kk) q[kk] = bf16x8{};
+      for (int kk = 0; kk < 4; ++kk) q[32 + kk] = load16(qp + 16 * kk);
     }
+
+    // Software pipeline over tiles (4 LDS stages): iteration `it` runs the
+    // QK^T MFMAs of tile it+1 interleaved with the softmax VALU work of tile
+    // it, then the PV MFMAs of tile it.  Tiles it and it+1 are resident, it+2
+    // and it+3 are in flight; the copy of tile it+3 goes into the stage tile
+    // it-1 used.  Every iteration issues exactly one tile of copies (past the
+    // end of the piece it repeats the last tile into a stage nobody reads), so
+    // every wait below has a fixed count.
+    static_assert(NSTAGE == 4, "the pipeline keeps two tiles resident and two in flight");
+    const int last_tile = ntiles - 1;
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      const int ti = min(st, last_tile);
+      const TilePages tp = checked(fetch_pages(kv0 + ti * kTile));
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i) dma(i, kv0 + ti * kTile, tp, smem + st * kStageBytes);
+    }
+    TilePages pg_raw = fetch_pages(kv0 + min(3, last_tile) * kTile);
+
+    // QK^T of one tile into acc (lane: head lane&31, 16 keys).  `extra(kk)`
+    // is called between the MFMAs so that independent VALU/VMEM work issues
+    // while the matrix pipe runs.
+    auto qk_tile = [&](const uint8_t* kb, f32x16& acc, auto&& extra) {
+      bf16x8 a[3];
+      auto read_k = [&](int kk) {
+        return *reinterpret_cast<const bf16x8*>(kb + qk_base[kk & 3] + 128 * (kk >> 2));
+      };
+      a[0] = read_k(0);
+      a[1] = read_k(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 36; ++kk) {
+        if (kk + 2 < 36) a[(kk + 2) % 3] = read_k(kk + 2);
+        extra(kk);
+        s_mfma(acc, a[kk % 3], q[kk], kk == 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_mfma_drain(acc);
+    };
+
+    // Tile 0 (and the query rows, loaded before it) have landed once two
+    // tiles of copies are still in flight.  The empty asm statements tie the
+    // query registers to this point: the loads fill them asynchronously, so
+    // nothing may read, copy or reuse them before the wait.
+    {
+      wait_vmem<2 * kLoadsPerWave>();
+      asm volatile("" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]), "+v"(q[6]),
+                   "+v"(q[7]), "+v"(q[8]));
+      asm volatile("" : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
+                   "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
+      asm volatile("" : "+v"(q[18]), "+v"(q[19]), "+v"(q[20]), "+v"(q[21]), "+v"(q[22]), "+v"(q[23]),
+                   "+v"(q[24]), "+v"(q[25]), "+v"(q[26]));
+      asm volatile("" : "+v"(q[27]), "+v"(q[28]), "+v"(q[29]), "+v"(q[30]), "+v"(q[31]), "+v"(q[32]),
+                   "+v"(q[33]), "+v"(q[34]), "+v"(q[35]));
+      if (!row_ok) {
+#pragma unroll
+        for (int kk = 0; kk < 36; ++kk) q[kk] = bf16x8{};
+      }
+      __syncthreads();
+    }
+    f32x16 s_cur;
+    qk_tile(smem, s_cur, [](int) {});
 
     float m_ref = -INFINITY;  // running reference max (log2 units), same in lanes l and l^32
     float l_part = 0.f;       // this lane's share of the running sum
 
     for (int it = 0; it < ntiles; ++it) {
-      wait_vmem_all();
-      __syncthreads();
       const bool has_next = it + 1 < ntiles;
-      const int tb = kv0 + it * TILE;
-      // Pages of tile it+1 (loaded during tile it-1); fetch those of tile it+2.
-      if (has_next) pg_next = checked(pg_raw);
-      if (it + 2 < ntiles) pg_raw = fetch_pages(tb + 2 * TILE);
+      // Tile it+1 has landed once only tile it+2's copies of this wave are in
+      // flight; the barrier publishes every wave's part and frees the stage of
+      // tile it-1 for the next copy.
+      wait_vmem<kLoadsPerWave>();
+      __syncthreads();
+
+      const int tb = kv0 + it * kTile;
+      const uint8_t* kb = smem + (it % NSTAGE) * kStageBytes;             // tile it (PV)
+      const uint8_t* kb_next = smem + ((it + 1) % NSTAGE) * kStageBytes;  // tile it+1 (QK^T)
+      const int nt = it + 3;                                              // tile to copy now
+      const int nti = min(nt, last_tile);
+      uint8_t* nbuf = smem + (nt % NSTAGE) * kStageBytes;
+      const TilePages npg = checked(pg_raw);
+      pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile);
       __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* kb = smem + (it & 1) * S::kBufBytes;
-      uint8_t* nb = smem + ((it + 1) & 1) * S::kBufBytes;
 
-      // The tile is processed in 32-key blocks: QK^T, softmax and PV per block
-      // (one block's scores and probabilities in registers at a time).
+      // ---- tile it: mask, scale to log2 units, tile max ----
+      const bool need_mask = tb + kTile > lim;
 #pragma unroll
-      for (int blk = 0; blk < S::kBlocks; ++blk) {
-        const uint8_t* kblk = kb + blk * 32 * kRowBytesLds;
-        const int t0 = tb + blk * 32;
-
-        // ---- S^T = K Q^T for 32 keys (lane: head lane&31, 16 keys); during the
-        //      first block the next tile's copies are issued between the MFMAs ----
-        f32x16 s;
-        bf16x8 a[3];
-        a[0] = *reinterpret_cast<const bf16x8*>(kblk + qk_off);
-        a[1] = *reinterpret_cast<const bf16x8*>(kblk + qk_off + 32);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < 36; ++kk) {
-          if (kk + 2 < 36) a[(kk + 2) % 3] = *reinterpret_cast<const bf16x8*>(kblk + qk_off + (kk + 2) * 32);
-          if (blk == 0 && kk < S::kLoadsPerWave && has_next) dma(kk, tb + TILE, pg_next, nb);
-          s_mfma(s, a[kk % 3], q[kk], kk == 0);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) {
+        float x = s_cur[i] * scale_log2;
+        if (need_mask) {
+          const int tok = tb + (i >> 2) * 8 + half * 4 + (i & 3);
+          x = tok < lim ? x : -INFINITY;
         }
-        s_mfma_drain(s);
-
-        // ---- mask, scale to log2 units, block max ----
-        const bool need_mask = t0 + 32 > lim;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[i] * scale_log2;
-          if (need_mask) {
-            const int tok = t0 + (i >> 2) * 8 + half * 4 + (i & 3);
-            x = tok < lim ? x : -INFINITY;
-          }
-          s[i] = x;
-          mx = fmaxf(mx, x);
-        }
-        mx = partner_max(mx);
-
-        // ---- lazy rescale of the running output ----
-        // A row moves its reference only when its maximum grows by more than
-        // kRescaleThreshold; the first finite maximum needs no rescale because
-        // nothing has been accumulated yet.
-        const bool need_update = mx > m_ref + kRescaleThreshold;
-        if (__any(need_update)) {
-          const bool need_scale = need_update && m_ref != -INFINITY;
-          const float m_new = need_update ? mx : m_ref;
-          const float alpha = need_scale ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-          l_part *= alpha;
-          if (__any(need_scale)) o_scale_all(alpha);
-          m_ref = m_new;
-        }
-        const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-        // ---- P = 2^(x - mu), as bf16 MFMA B operands, 8 keys per 16-key step ----
-        bf16x8 pb[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[i] - mu);
-          l_part += p;
-          pb[i >> 3][i & 7] = (__bf16)p;
-        }
-        // Materialize the bf16 operands here, not next to the MFMAs.
-        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- O^T += V^T P^T, V^T read transposed from the same block ----
-        i16x8 v[3];
-        auto read_v = [&](int idx) {
-          const int ks = idx >> 4, cb = idx & 15;
-          const uint8_t* vb = kblk + pv_off + ks * 16 * kRowBytesLds + cb * 64;
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, vb));
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, vb + 8 * kRowBytesLds));
-          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        v[0] = read_v(0);
-        v[1] = read_v(1);
-        asm volatile("s_nop 4" ::: );
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int idx = 0; idx < 32; ++idx) {
-          if (idx + 2 < 32) v[(idx + 2) % 3] = read_v(idx + 2);
-          const int ks = idx >> 4, cb = idx & 15;
-          o_mfma(cb, __builtin_bit_cast(bf16x8, v[idx % 3]), pb[ks], it == 0 && blk == 0 && ks == 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        s_cur[i] = x;
       }
+      float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
+                       fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
+                           fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
+      mx = partner_max(mx);
+
+      // ---- lazy rescale of the running output ----
+      // A row moves its reference only when its maximum grows by more than
+      // kRescaleThreshold; the first finite maximum needs no rescale because
+      // nothing has been accumulated yet.
+      const bool need_update = mx > m_ref + kRescaleThreshold;
+      if (__any(need_update)) {
+        const bool need_scale = need_update && m_ref != -INFINITY;
+        const float m_new = need_update ? mx : m_ref;
+        const float alpha = need_scale ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        l_part *= alpha;
+        if (__any(need_scale)) o_scale_all(alpha);
+        m_ref = m_new;
+      }
+      const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- QK^T of tile it+1, with P = 2^(x - mu) of tile it (bf16 MFMA B
+      //      operands, 8 keys per 16-key step) and the copies of tile it+3
+      //      issued between its MFMAs ----
+      bf16x8 pb[2];
+      auto softmax_step = [&](int kk) {
+        if (kk < 16) {
+          const float p = __builtin_amdgcn_exp2f(s_cur[kk] - mu);
+          l_part += p;
+          pb[kk >> 3][kk & 7] = (__bf16)p;
+        }
+        if (kk >= 16 && kk < 16 + kLoadsPerWave) dma(kk - 16, kv0 + nti * kTile, npg, nbuf);
+      };
+      f32x16 s_next;
+      if (has_next) {
+        qk_tile(kb_next, s_next, softmax_step);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 36; ++kk) softmax_step(kk);
+      }
+      // Materialize the bf16 operands here, not next to the MFMAs.
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- O^T += V^T P^T for tile it, V^T read transposed from its stage ----
+      i16x8 v[3];
+      auto read_v = [&](int idx) {
+        const int ks = idx >> 4, cb = idx & 15;
+        const uint8_t* v0p = kb + pv_base[0][cb & 1] + 18432 * ks + 128 * (cb >> 1);
+        const uint8_t* v1p = kb + pv_base[1][cb & 1] + 18432 * ks + 128 * (cb >> 1);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, v0p));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, v1p));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      v[0] = read_v(0);
+      v[1] = read_v(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int idx = 0; idx < 32; ++idx) {
+        if (idx + 2 < 32) v[(idx + 2) % 3] = read_v(idx + 2);
+        const int ks = idx >> 4, cb = idx & 15;
+        o_mfma(cb, __builtin_bit_cast(bf16x8, v[idx % 3]), pb[ks], it == 0 && ks == 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_cur = s_next;
     }
+
+    // The repeated copies past the end of the piece must land before the next
+    // piece reuses their stages.
+    wait_vmem<0>();
 
     // ---- epilogue: normalize and store (final output or a workspace partial) ----
     o_drain();
@@ -438,8 +515,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
         dl = lse + (int64_t)b * rows + row;
       } else {
         const int64_t slot = (int64_t)sg.partial * nrb + rb;
-        dst = ws_o + (slot * S::kRowsPerBlock + row_local) * 512;
-        dl = ws_lse + slot * S::kRowsPerBlock + row_local;
+        dst = ws_o + (slot * kRowsPerBlock + row_local) * 512;
+        dl = ws_lse + slot * kRowsPerBlock + row_local;
       }
       o_store_rec<0>(dst, half, inv);
       if (half == 0) *dl = lse_v;
@@ -621,7 +698,7 @@ mla_status check_device(const mla_plan* plan) {
   return MLA_OK;
 }
 
-template <int NW, int TILE, bool SINGLE_PAGE>
+template <int NSTAGE, bool SINGLE_PAGE>
 hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* cache,
                          int64_t num_pages, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
                          float scale_log2, float* out, float* lse, float* ws_o, float* ws_lse,
@@ -630,7 +707,7 @@ hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q
   const char* base = static_cast<const char*>(plan->dev);
   int page_log2 = 0;
   while ((1 << page_log2) < d.page) ++page_log2;
-  hipLaunchKernelGGL((mla::decode_kernel<NW, TILE, SINGLE_PAGE>), dim3(d.grid), dim3(64 * NW), 0, stream,
+  hipLaunchKernelGGL((mla::decode_kernel<NSTAGE, SINGLE_PAGE>), dim3(d.grid), dim3(64 * mla::kWaves), 0, stream,
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
                      static_cast<const uint8_t*>(cache), num_pages, bt, bt_stride, seq_lens,
                      reinterpret_cast<const int32_t*>(base + plan->off_lens),
@@ -739,17 +816,11 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;
   const bool single = d.page >= d.v.tile_tokens;
-  hipError_t e;
-#define MLA_LAUNCH(NW, TILE, SP)                                                                                 \
-  launch_decode<NW, TILE, SP>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens, \
-                              scale_log2, out, lse, ws_o, ws_lse, st)
-  if (d.v.waves == 4 && d.v.tile_tokens == 64)
-    e = single ? MLA_LAUNCH(4, 64, true) : MLA_LAUNCH(4, 64, false);
-  else if (d.v.waves == 2 && d.v.tile_tokens == 32)
-    e = single ? MLA_LAUNCH(2, 32, true) : MLA_LAUNCH(2, 32, false);
-  else
-    return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
-#undef MLA_LAUNCH
+  if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile) return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
+  hipError_t e = single ? launch_decode<4, true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
+                                                 seq_lens, scale_log2, out, lse, ws_o, ws_lse, st)
+                        : launch_decode<4, false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
+                                                  bt_stride, seq_lens, scale_log2, out, lse, ws_o, ws_lse, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   g_last_error.clear();
   return MLA_OK;

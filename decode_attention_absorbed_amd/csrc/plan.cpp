@@ -125,16 +125,13 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
   p.page = page;
   p.num_cus = num_cus;
   p.rows = q_len * heads;
-  int variant = tuning.variant;
-  if (variant == 0) variant = 1;
-  if (variant == 1) {
-    p.v = Variant{4, 64, 1};
-  } else if (variant == 2) {
-    p.v = Variant{2, 32, 2};
-  } else {
+  // One kernel shape: 4 waves (128 query rows) per workgroup, 32-key tiles,
+  // one workgroup per compute unit (its LDS ring takes 144 KB).
+  if (tuning.variant != 0 && tuning.variant != 1) {
     *err = "unknown kernel variant";
     return kInvalid;
   }
+  p.v = Variant{4, 32, 1};
   p.nrb = (p.rows + p.v.rows_per_block() - 1) / p.v.rows_per_block();
   p.lens.assign(lens, lens + batch);
   for (int32_t b = 0; b < batch; ++b) p.max_pages = std::max(p.max_pages, (lens[b] + page - 1) / page);

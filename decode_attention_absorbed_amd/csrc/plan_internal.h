@@ -55,9 +55,9 @@ struct PlanData {
 
 // Tunables of the planner (exposed for tests; defaults used by the ABI).
 struct PlanTuning {
-  double seg_overhead_tiles = 4.0;  // cost of one extra piece, in tiles
-  double min_fragment_tiles = 2.0;  // do not start a piece smaller than this when splitting
-  int32_t variant = 0;              // 0 = automatic, 1 = 4 waves x 64 keys, 2 = 2 waves x 32 keys
+  double seg_overhead_tiles = 8.0;  // cost of one extra piece, in 32-key tiles
+  double min_fragment_tiles = 4.0;  // do not start a piece smaller than this when splitting
+  int32_t variant = 0;              // 0 = automatic; 1 = 4 waves x 32-key tiles (the only kernel)
 };
 
 // Validate and build the host schedule.  Returns 0 on success, otherwise an
