@@ -4,30 +4,37 @@
 // The computation (Huawei, "DeepSeek V3/R1 inference deployment best practices
 // on Ascend servers", section 3.2.1 and section 6.1): every head of a request
 // attends over the same cached 576-wide rows [c_kv | k_pe]; V is c_kv.  With
-// the heads as the M dimension, QK^T and PV are dense contractions against a
-// shared key tile, so both run on bf16 MFMA with fp32 accumulation.
+// the heads as one dimension of the product, QK^T and PV are dense
+// contractions against a shared key tile, so both run on bf16 MFMA with fp32
+// accumulation.
 //
 // Decode kernel: one workgroup = 4 waves = 128 query rows (rows are the
 // flattened (query token, head) pairs of one request), walking one or more
 // pieces of key range in tiles of 32 keys:
 //  * tiles are copied HBM -> LDS with 16-byte direct loads
-//    (global_load_lds_dwordx4) into a ring of NSTAGE buffers; while tile i is
-//    computed, tiles i+1 .. i+NSTAGE-1 are in flight (about 110 KB per CU, to
-//    cover HBM latency at full bandwidth).  One barrier per tile;
+//    (global_load_lds_dwordx4) into a ring of 4 buffers; while tile i is
+//    computed, tiles i+1 .. i+3 are resident or in flight (about 110 KB per
+//    CU, enough to cover HBM latency at full bandwidth).  One barrier per tile;
 //  * a cached row is 72 chunks of 16 bytes; inside each aligned group of 8
 //    chunks, chunk c of key row t is stored at c ^ swz(t).  The swizzle makes
 //    both the row reads of QK^T (16 rows, same chunk) and the transposed reads
-//    of PV (4 rows x 4 chunks) hit 16 distinct 4-bank groups;
-//  * wave w keeps its 32 query rows, as the B operand of
-//    v_mfma_f32_32x32x16_bf16, in 144 VGPRs for the whole piece, and computes
-//    S^T = K Q^T for the tile's 32 keys (A operand = key rows read from LDS);
-//    in that layout each lane holds one head and 16 keys, so the row maximum
-//    needs one cross-half swap and the running (max, sum) is lane-local;
+//    of PV (8 rows x 2 chunks per half wave) hit distinct banks;
+//  * all products are v_mfma_f32_16x16x32_bf16.  (The 32x32x16 form needs a
+//    36-step dependent chain per tile for QK^T, which runs at a third of the
+//    matrix rate; the 16x16 form gives four independent 18-step chains, and a
+//    K of 32 lets one PV product cover a whole tile.)
+//  * wave w owns 32 query rows as two blocks of 16 (hb = 0, 1).  Its query
+//    rows stay in 144 VGPRs as the B operand for the whole piece.
+//    S^T = K Q^T for the tile: 2 key blocks x 2 row blocks; lane l holds rows
+//    16hb + l%16 and keys 16kb + 4(l/16) + 0..3, so the row maximum and sum
+//    reduce over the four 16-lane groups (two lane swaps);
 //  * online softmax in base 2 with a lazy reference: the output is rescaled
 //    only when a row's maximum grows by more than 2^8;
-//  * O^T = V^T P^T accumulates in 16 MFMA tiles (256 registers, AGPR); V^T
-//    comes straight from the same LDS tile through ds_read_b64_tr_b16 (the
-//    c_kv columns of the key rows; no second copy of V);
+//  * O^T = V^T P^T accumulates in 64 MFMA blocks of 16 columns x 16 rows
+//    (256 registers, AGPR).  P^T is built in registers from the S^T lane
+//    layout (K slot 8g + j of lane group g stands for key 4g + j, j < 4, and
+//    key 16 + 4g + j - 4 otherwise); V^T comes straight from the same LDS
+//    tile through ds_read_b64_tr_b16 in that key order (no second copy of V);
 //  * the piece ends with out = O / l and lse = ln(sum) written either to the
 //    final tensors (a request in one piece) or to a workspace partial.
 // Combine kernel: per split request and row, lse = logsumexp over its pieces,
@@ -40,6 +47,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
 
 #include "mla_decode.h"
 #include "plan_internal.h"
@@ -48,9 +56,9 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -61,25 +69,61 @@ constexpr int kTile = 32;           // keys per tile
 constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = 32 * kWaves;
 constexpr int kStageBytes = kTile * kRowBytes;         // 36864
+constexpr int kStages = 4;                             // LDS tile ring
+constexpr int kSoftmaxSteps = 28;                      // pieces of the per-tile softmax
 constexpr int kLoadsPerTile = kTile * kChunks / 64;     // 36 one-KB copies
 constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;  // 9
+constexpr int kQSteps = 576 / 32;                      // 18 K steps of QK^T
+constexpr int kNopeSteps = 512 / 32;                   // the first 16 come from c_kv
+constexpr int kQpeWaveBytes = 32 * 64 * 2;             // q_pe of one wave's 32 rows in LDS
+#ifndef MLA_QK_DEPTH
+#define MLA_QK_DEPTH 2
+#endif
+#ifndef MLA_PV_DEPTH
+#define MLA_PV_DEPTH 3
+#endif
+constexpr int kQkDepth = MLA_QK_DEPTH;  // K steps of LDS reads in flight ahead of the QK^T MFMAs
+constexpr int kPvDepth = MLA_PV_DEPTH;  // column blocks of V^T reads in flight ahead of the PV MFMAs
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of copies");
 
-// Chunk swizzle of key row t (t = row within the tile).
-__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+// LDS layout of a 32-key tile (36 KB), column major: the 16-byte chunk c
+// (0..71) of key row t (0..31) sits at slot 32c + (t ^ 8(c & 1)).
+//  * a 1 KB copy n fills slots 64n .. 64n+63: lane l brings chunk 2n + l/32 of
+//    key row (l % 32) ^ 8(l / 32), so a lane's source row is the same for every
+//    copy and the copies of a tile differ only by a constant offset;
+//  * QK^T reads 16 consecutive key rows of one chunk per 16 lanes (256
+//    contiguous bytes);
+//  * PV's transposed reads take 8 rows x 2 chunks per half wave; the row xor
+//    on odd chunks puts the two chunks on different banks.
 
-__device__ __forceinline__ float partner_max(float x) {
-  // permlane32_swap(x, x) returns {lanes 0-31: x, 32-63: x of lane-32} and
-  // {lanes 0-31: x of lane+32, 32-63: x}; the max/sum of the pair is symmetric.
+// Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// permlaneX_swap(x, x) returns the pair {x[l & ~X], x[l | X]} in some order,
+// so combining its two results is symmetric in the pair.
+// max of three floats in one instruction (the compiler's fmaxf adds NaN
+// canonicalization around every operand; v_max3_f32 treats NaN like fmaxf).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float group_max32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float partner_sum(float x) {
+__device__ __forceinline__ float group_max16(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+__device__ __forceinline__ float group_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -106,8 +150,20 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
 }
 
+// Same with a 64-bit per-lane address plus an immediate byte offset.  The
+// immediate offset moves the LDS destination too (lane l writes LDS byte
+// M0 + OFF + 16 l), so callers pass M0 = destination - OFF.
+template <int OFF>
+__device__ __forceinline__ void dma16_off(const void* src, uint32_t lds_dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "{m0}"(lds_dst), "n"(OFF) : "memory");
+}
+
+// Same with a uniform base, a 32-bit per-lane offset and an immediate offset
+// (which, as above, is added to the LDS destination as well).
+template <int OFF>
 __device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_dst) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(off), "s"(base), "{m0}"(lds_dst), "n"(OFF)
+               : "memory");
 }
 
 // 16-byte global load into VGPRs, invisible to the compiler's wait counts
@@ -123,82 +179,85 @@ __device__ __forceinline__ bf16x8 load16(const void* src) {
 // itself puts both in AGPRs and spills.  So the QK^T MFMA is issued as inline
 // asm with a VGPR constraint.  The hazards the compiler cannot see inside the
 // asm are handled here: the first step takes srcC = 0 (no VALU write of the
-// accumulator right before an MFMA reads it), and s_mfma_drain waits out the
+// accumulator right before an MFMA reads it; early clobber so the result does
+// not share registers with an operand), and s_mfma_drain waits out the
 // XDL-write -> VALU-read latency before anything reads the results.  Every
 // MFMA issued as asm starts with s_nop 1: a VALU write of a source register
 // needs two wait states before an MFMA reads it.
-__device__ __forceinline__ void s_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
+__device__ __forceinline__ void s_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b, bool first) {
   if (first)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-__device__ __forceinline__ void s_mfma_drain(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc)); }
+__device__ __forceinline__ void s_mfma_drain(f32x4 (&acc)[4]) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+}
 
-// The output accumulators O^T (16 tiles of 32x32 fp32 = 256 registers per
-// lane) live in the physical AGPRs a[0:255]: tile cb is a[16cb : 16cb+15].
-// They are only touched by inline asm that names them and lists them as
-// clobbered, so the compiler never allocates them (left to itself it carries
-// them through VGPRs around the rare rescale branch and spills the query rows).
-// Hazards the compiler cannot see are handled where the code runs:
+// The output accumulators O^T (64 blocks of 16x16 fp32 = 256 registers per
+// lane) live in the physical AGPRs a[0:255]: block n = 2 * cb + hb (columns
+// 16cb .. 16cb+15, row block hb) is a[4n : 4n+3].  Lane l of block n holds
+// row 16hb + l%16, columns 16cb + 4(l/16) + 0..3.  They are only touched by
+// inline asm that names them and lists them as clobbered, so the compiler
+// never allocates them (left to itself it carries them through VGPRs around
+// the rare rescale branch and spills the query rows).  Hazards the compiler
+// cannot see are handled where the code runs:
 //  * MFMA -> accvgpr_read of the results: o_drain waits 24 wait states;
 //  * accvgpr_write (rescale) -> MFMA srcC: the whole softmax runs in between,
 //    plus the s_nop in front of every MFMA.
-template <int CB>
-struct OTile;
+template <int N>
+struct OBlock;
 template <int N>
 __device__ __forceinline__ float o_get();
 template <int N>
 __device__ __forceinline__ void o_set(float x);
 #include "agpr_tiles.inc"
 
-// Dispatch on a tile index that is a constant after unrolling.
-__device__ __forceinline__ void o_mfma(int cb, const bf16x8& a, const bf16x8& b, bool first) {
-#define MLA_CASE(n)               \
-  case n:                         \
-    if (first)                    \
-      OTile<n>::mfma_first(a, b); \
-    else                          \
-      OTile<n>::mfma(a, b);       \
-    break;
-  switch (cb) {
-    MLA_CASE(0) MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7)
-    MLA_CASE(8) MLA_CASE(9) MLA_CASE(10) MLA_CASE(11) MLA_CASE(12) MLA_CASE(13) MLA_CASE(14) MLA_CASE(15)
-  }
-#undef MLA_CASE
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: loop bodies whose
+// register names must be compile-time constants.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int N>
-__device__ __forceinline__ void o_scale_rec(float alpha) {
-  if constexpr (N < 256) {
-    o_set<N>(o_get<N>() * alpha);
-    o_scale_rec<N + 1>(alpha);
+// Zero all 256 accumulators (start of a piece).
+template <int R>
+__device__ __forceinline__ void o_zero_rec() {
+  if constexpr (R < 256) {
+    o_set<R>(0.f);
+    o_zero_rec<R + 1>();
   }
 }
 
-// Multiply all 256 accumulators by this lane's alpha.
-__device__ __forceinline__ void o_scale_all(float alpha) { o_scale_rec<0>(alpha); }
+// Multiply the accumulators of row block 0 by alpha0 and of row block 1 by
+// alpha1 (register r belongs to block r / 4, row block (r / 4) % 2).
+template <int R>
+__device__ __forceinline__ void o_scale_rec(float alpha0, float alpha1) {
+  if constexpr (R < 256) {
+    o_set<R>(o_get<R>() * (((R >> 2) & 1) ? alpha1 : alpha0));
+    o_scale_rec<R + 1>(alpha0, alpha1);
+  }
+}
+
+__device__ __forceinline__ void o_scale_all(float alpha0, float alpha1) { o_scale_rec<0>(alpha0, alpha1); }
 
 // Wait out the MFMA write -> AGPR read latency before reading results.
 __device__ __forceinline__ void o_drain() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
 
-// Store tile register group [4g, 4g+3] of tile cb (lane: 4 consecutive columns), scaled.
-template <int CB, int G>
-__device__ __forceinline__ void o_store4(float* dst, float inv) {
-  constexpr int n = 16 * CB + 4 * G;
-  f32x4 w = {o_get<n + 0>() * inv, o_get<n + 1>() * inv, o_get<n + 2>() * inv, o_get<n + 3>() * inv};
-  *reinterpret_cast<f32x4*>(dst) = w;
-}
-
-template <int CB>
-__device__ __forceinline__ void o_store_rec(float* dst, int half, float inv) {
-  if constexpr (CB < 16) {
-    o_store4<CB, 0>(dst + CB * 32 + 0 * 8 + 4 * half, inv);
-    o_store4<CB, 1>(dst + CB * 32 + 1 * 8 + 4 * half, inv);
-    o_store4<CB, 2>(dst + CB * 32 + 2 * 8 + 4 * half, inv);
-    o_store4<CB, 3>(dst + CB * 32 + 3 * 8 + 4 * half, inv);
-    o_store_rec<CB + 1>(dst, half, inv);
+// Store the 32 blocks of row block HB, scaled: block (cb, HB) goes to
+// dst[16cb .. 16cb+3] (dst already points at this lane's 4 columns).
+template <int HB, int CB>
+__device__ __forceinline__ void o_store_rec(float* dst, float inv) {
+  if constexpr (CB < 32) {
+    constexpr int r = 4 * (2 * CB + HB);
+    f32x4 w = {o_get<r + 0>() * inv, o_get<r + 1>() * inv, o_get<r + 2>() * inv, o_get<r + 3>() * inv};
+    *reinterpret_cast<f32x4*>(dst + 16 * CB) = w;
+    o_store_rec<HB, CB + 1>(dst, inv);
   }
 }
 
@@ -210,7 +269,7 @@ struct TilePages {
   int pg[2];
 };
 
-template <int NSTAGE, bool SINGLE_PAGE>
+template <bool SINGLE_PAGE>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint8_t* __restrict__ cache, int64_t num_pages,
@@ -220,50 +279,61 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_lse) {
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2..4 LDS stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * kStageBytes];
+  // 4 tile stages (144 KB) + the rope part of the query rows (16 KB): the
+  // 160 KB of LDS a workgroup may hold.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kWaves * kQpeWaveBytes];
+  uint8_t* const qpe_lds = smem + kStages * kStageBytes;
 
   const WorkgroupRange wr = wgs[blockIdx.x];
   if (wr.seg_begin >= wr.seg_end) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5;  // which 8-wide k slice of an MFMA operand this lane holds
+  const int grp = lane >> 4;  // 16-lane group: K slice of operands, row quad of results
+  const int l16 = lane & 15;
   const int rb = wr.row_block;
-  const int row_local = wave * 32 + (lane & 31);
-  const int row = rb * kRowsPerBlock + row_local;
-  const bool row_ok = row < rows;
-  const int jq = row_ok ? row / heads : 0;  // query token of this row
   const int psize = 1 << page_log2;
 
-  // Per-lane LDS byte offsets (within a stage) of the operand reads.
-  // QK^T, A operand = key rows: key t = lane & 31, logical chunk 2*kk + half,
-  // stored at chunk (2*kk + half) ^ swz(t) of its 8-group.  For kk = 4*g + m
-  // the offset is qk_base[m] + 128*g.
-  int qk_base[4];
-  {
-    const int t = lane & 31;
+  // This lane's two query rows: row block hb of the wave, row l16 in it.
+  int row_local[2], row[2], jq[2];
+  bool row_ok[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qk_base[m] = t * kRowBytes + 16 * ((2 * m + half) ^ swz(t));
+  for (int hb = 0; hb < 2; ++hb) {
+    row_local[hb] = wave * 32 + hb * 16 + l16;
+    row[hb] = rb * kRowsPerBlock + row_local[hb];
+    row_ok[hb] = row[hb] < rows;
+    jq[hb] = row_ok[hb] ? row[hb] / heads : 0;  // query token of the row
   }
-  // PV, A operand = V^T via transposed reads: within each 16-lane group g, lane k
-  // addresses key row (k / 4) of a 4-key strip, columns 4 * (k % 4) .. + 3 of a
-  // 16-column strip; the read hands lane k column k of the 4 x 16 block.  Key
-  // row r = 16*ks + 8*qq + 4*half + k/4, column 32*cb + 16*(g&1) + 4*(k&3); its
-  // chunk (column / 8) is swizzled by the row.  The offset is
-  // pv_base[qq][cb&1] + 18432*ks + 128*(cb>>1).
-  int pv_base[2][2];
-  {
-    const int grp = lane >> 4, k16 = lane & 15;
-    const int clow = 2 * (grp & 1) + ((k16 & 3) >> 1);  // chunk within a 4-chunk (32-column) group
+  // The wave's first row has the fewest visible keys; a wave with rows past
+  // the end masks every tile.
+  const int wave_row0 = rb * kRowsPerBlock + wave * 32;
+  const bool wave_full = wave_row0 + 31 < rows;
+  const int wave_jq0 = wave_row0 / heads;
+
+  // Per-lane LDS byte offsets (within a stage) of the operand reads; the
+  // remaining terms are compile-time offsets.
+  // QK^T, A operand = key rows: key 16kb + l16, chunk 4ks + grp:
+  //   qk_base + 2048 ks + 256 kb.
+  const int qk_off = 512 * grp + 16 * (l16 ^ (8 * (grp & 1)));
+  // PV, A operand = V^T via transposed reads.  Within 16-lane group grp, lane
+  // l16 addresses key row 16rd + 4grp + l16/4, columns 16cb + 4(l16%4) .. +3
+  // (chunk 2cb + (l16%4)/2, byte 8(l16%2)); the read hands it column 16cb + l16
+  // of those 4 keys (K slots 4rd .. 4rd+3 of the group):
+  //   pv_base + 1024 cb + 256 rd.
+  const int hsel = (l16 >> 1) & 1;
+  const int pv_off = 512 * hsel + 16 * ((4 * grp + (l16 >> 2)) ^ (8 * hsel)) + 8 * (l16 & 1);
+  // Tile copies: wave w issues copies n = 4i + w (i = 0..8) of a tile; lane l
+  // reads key row dma_row, bytes dma_col + 128 i of it.
+  const int dma_row = (lane & 31) ^ (8 * (lane >> 5));
+  const int dma_col = 16 * (lane >> 5) + 32 * wave;
+  // Rope part of the query (dims 512..575) in LDS: row r (0..31) of wave w
+  // at w * 4096 + 128 r, its 16-byte chunk c at slot c ^ ((r >> 1) & 7), so
+  // that 16 rows reading one chunk hit distinct banks.  B operand of step
+  // 16 + e, row block hb: row 16hb + l16, chunk 4e + grp.
+  int qpe_base[2];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int r = 8 * qq + 4 * half + (k16 >> 2);
-#pragma unroll
-      for (int odd = 0; odd < 2; ++odd)
-        pv_base[qq][odd] = r * kRowBytes + 16 * ((4 * odd + clow) ^ swz(r)) + 8 * (k16 & 1);
-    }
-  }
+  for (int e = 0; e < 2; ++e)
+    qpe_base[e] = (int)lds_addr(qpe_lds) + wave * kQpeWaveBytes + l16 * 128 + 16 * ((4 * e + grp) ^ ((l16 >> 1) & 7));
 
   for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
     const Segment sg = segs[si];
@@ -272,8 +342,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const bool bad_len = (L != planned_lens[b]);
     const int32_t* bt_row = block_table + (int64_t)b * bt_stride;
 
-    // Keys this row may see inside the piece: [kv0, lim).
-    const int lim = row_ok ? min(kv1, L - q_len + 1 + jq) : kv0;
+    // Keys each of this lane's rows may see inside the piece: [kv0, lim).
+    int lim[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) lim[hb] = row_ok[hb] ? min(kv1, L - q_len + 1 + jq[hb]) : kv0;
+    // A tile starting at key tb needs masking iff tb + kTile > lim_wave.
+    const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
 
     // Block-table entries of a tile (scalar loads, checked when used).
     auto fetch_pages = [&](int tb) {
@@ -290,27 +364,40 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       return tp;
     };
 
-    // Copy i of this wave for the tile at key tb: LDS slots [64 n, 64 n + 64)
-    // of the stage, n = i * 4 + wave; slot p holds chunk (p % 72) ^ swz of key
-    // p / 72.  Keys past the piece are clamped to its last key (their scores
-    // are masked; the copy stays inside the request's pages).
-    auto dma = [&](int i, int tb, const TilePages& tp, uint8_t* stage) {
-      const int n = i * kWaves + wave;
-      int lane_v = lane;
-      asm volatile("" : "+v"(lane_v));  // keep the address math next to its use
-      const int pos = n * 64 + lane_v;
-      const int t = pos / kChunks;
-      const int pc = pos - t * kChunks;
-      const int c = pc ^ swz(t);
-      const int tok = min(tb + t, kv1 - 1);
-      const uint32_t lds_dst = lds_addr(stage + n * 1024);
+    // Per-tile source of this lane's copies.  Key rows past the piece are
+    // clamped to its last key: their scores are masked, and the copy stays
+    // inside the request's pages with finite values for PV.
+    struct TileSrc {
+      const uint8_t* base;  // uniform (one page per tile)
+      uint32_t off;         // per lane
+      const uint8_t* ptr;   // per lane (two pages per tile)
+    };
+    auto tile_src = [&](int tb, const TilePages& tp) {
+      TileSrc ts;
+      const int tok = min(tb + dma_row, kv1 - 1);
       if (SINGLE_PAGE) {
-        const uint8_t* pbase = cache + ((int64_t)tp.pg[0] << page_log2) * kRowBytes;
-        dma16_saddr(pbase, (uint32_t)((tok & (psize - 1)) * kRowBytes + c * 16), lds_dst);
+        ts.base = cache + ((int64_t)tp.pg[0] << page_log2) * kRowBytes;
+        ts.off = (uint32_t)((tok & (psize - 1)) * kRowBytes + dma_col);
+        ts.ptr = nullptr;
       } else {
         const int page = ((tok >> page_log2) == tp.first) ? tp.pg[0] : tp.pg[1];
-        dma16(cache + (((int64_t)page << page_log2) + (tok & (psize - 1))) * kRowBytes + c * 16, lds_dst);
+        ts.base = nullptr;
+        ts.off = 0;
+        ts.ptr = cache + (((int64_t)page << page_log2) + (tok & (psize - 1))) * kRowBytes + dma_col;
       }
+      return ts;
+    };
+    // Copy i (0..8) of this wave for a tile into `stage`.
+    auto dma = [&](auto ic, const TileSrc& ts, uint8_t* stage) {
+      constexpr int i = decltype(ic)::value;
+      const uint32_t dst = lds_addr(stage) + (uint32_t)((4 * i + wave) * 1024 - 128 * i);
+      if (SINGLE_PAGE)
+        dma16_saddr<128 * i>(ts.base, ts.off, dst);
+      else
+        dma16_off<128 * i>(ts.ptr, dst);
+    };
+    auto dma_all = [&](const TileSrc& ts, uint8_t* stage) {
+      static_for<kLoadsPerWave>([&](auto ic) { dma(ic, ts, stage); });
     };
 
     const int ntiles = (kv1 - kv0 + kTile - 1) / kTile;
@@ -319,56 +406,179 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // tiles of this one land in LDS.
     __syncthreads();
 
-    // Query rows as the MFMA B operand: lane holds dims 16*kk + 8*half .. +7.
-    // Issued first so that the wait for tile 0 also covers them.
-    bf16x8 q[36];
-    {
-      const int qrow = row_ok ? row : 0;  // rows past the end load row 0 and are zeroed below
-      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * half;
-      const uint16_t* qp = q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * half;
+    // Query rows as the B operand: q[16hb + ks] holds dims 32ks + 8grp .. +7
+    // of row hb (c_kv part, registers); the rope part is copied to this
+    // wave's LDS slice (4 copies of 1 KB: slot p = row p/8, chunk p%8).  Rows
+    // past the end load row 0: their scores are masked and they are never
+    // stored.  Issued first so that the wait for tile 0 also covers them.
+    bf16x8 q[2 * kNopeSteps];
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) q[kk] = load16(qn + 16 * kk);
+    for (int hb = 0; hb < 2; ++hb) {
+      const int qrow = row_ok[hb] ? row[hb] : 0;
+      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * grp;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[32 + kk] = load16(qp + 16 * kk);
+      for (int ks = 0; ks < kNopeSteps; ++ks) q[kNopeSteps * hb + ks] = load16(qn + 32 * ks);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int pidx = n * 64 + lane;
+      const int r = pidx >> 3;
+      const int c = (pidx & 7) ^ ((r >> 1) & 7);
+      const int qr = wave_row0 + r;
+      const int qrow = qr < rows ? qr : 0;
+      dma16(q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * c, lds_addr(qpe_lds + wave * kQpeWaveBytes + n * 1024));
     }
 
-    // Software pipeline over tiles (4 LDS stages): iteration `it` runs the
-    // QK^T MFMAs of tile it+1 interleaved with the softmax VALU work of tile
-    // it, then the PV MFMAs of tile it.  Tiles it and it+1 are resident, it+2
-    // and it+3 are in flight; the copy of tile it+3 goes into the stage tile
-    // it-1 used.  Every iteration issues exactly one tile of copies (past the
-    // end of the piece it repeats the last tile into a stage nobody reads), so
-    // every wait below has a fixed count.
-    static_assert(NSTAGE == 4, "the pipeline keeps two tiles resident and two in flight");
+    // Software pipeline over tiles (4 LDS stages).  Iteration `it`:
+    //   QK^T of tile it+1, with the copies of tile it+3 issued between its
+    //   MFMAs (into the stage tile it-1 used);
+    //   PV of tile it, with the softmax of tile it+1 (mask, row max, lazy
+    //   reference update, P) issued between its MFMAs;
+    //   the rare rescale of O when a row's reference moved.
+    // Tiles it and it+1 are resident, it+2 and it+3 in flight.  Every
+    // iteration issues exactly one tile of copies (past the end of the piece
+    // it repeats the last tile into a stage nobody reads), so every wait below
+    // has a fixed count.
     const int last_tile = ntiles - 1;
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
       const int ti = min(st, last_tile);
-      const TilePages tp = checked(fetch_pages(kv0 + ti * kTile));
-#pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) dma(i, kv0 + ti * kTile, tp, smem + st * kStageBytes);
+      const int tb_c = kv0 + ti * kTile;
+      dma_all(tile_src(tb_c, checked(fetch_pages(tb_c))), smem + st * kStageBytes);
     }
     TilePages pg_raw = fetch_pages(kv0 + min(3, last_tile) * kTile);
 
-    // QK^T of one tile into acc (lane: head lane&31, 16 keys).  `extra(kk)`
-    // is called between the MFMAs so that independent VALU/VMEM work issues
-    // while the matrix pipe runs.
-    auto qk_tile = [&](const uint8_t* kb, f32x16& acc, auto&& extra) {
-      bf16x8 a[3];
-      auto read_k = [&](int kk) {
-        return *reinterpret_cast<const bf16x8*>(kb + qk_base[kk & 3] + 128 * (kk >> 2));
+    // QK^T of one tile: acc[2kb + hb] = S^T block (keys 16kb.., rows 16hb..).
+    // `extra(k)` (k = 4ks + j) is called between the MFMAs so that
+    // independent work issues while the matrix pipe runs.
+    auto qk_tile = [&](const uint8_t* kb, f32x4(&acc)[4], auto&& extra) {
+      constexpr int D = kQkDepth;
+      bf16x8 a[D + 1][2];
+      bf16x8 qb[2][2];  // rope steps: [e][hb]
+      auto read_step = [&](int ks) {
+        a[ks % (D + 1)][0] = *reinterpret_cast<const bf16x8*>(kb + qk_off + 2048 * ks);
+        a[ks % (D + 1)][1] = *reinterpret_cast<const bf16x8*>(kb + qk_off + 2048 * ks + 256);
+        if (ks >= kNopeSteps) {
+          const int e = ks - kNopeSteps;
+          qb[e][0] = *LDS_AS(const bf16x8, (uintptr_t)qpe_base[e]);
+          qb[e][1] = *LDS_AS(const bf16x8, (uintptr_t)(qpe_base[e] + 2048));
+        }
       };
-      a[0] = read_k(0);
-      a[1] = read_k(1);
+#pragma unroll
+      for (int d = 0; d < D; ++d) read_step(d);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < 36; ++kk) {
-        if (kk + 2 < 36) a[(kk + 2) % 3] = read_k(kk + 2);
-        extra(kk);
-        s_mfma(acc, a[kk % 3], q[kk], kk == 0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < kQSteps; ++ks) {
+        if (ks + D < kQSteps) read_step(ks + D);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          extra(4 * ks + j);
+          const bf16x8& bq = ks < kNopeSteps ? q[kNopeSteps * (j & 1) + ks] : qb[ks - kNopeSteps][j & 1];
+          s_mfma(acc[j], a[ks % (D + 1)][j >> 1], bq, ks == 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       s_mfma_drain(acc);
+    };
+
+    // O^T += V^T P^T for one tile, V^T read transposed from its stage;
+    // `extra(cb)` is called between the two MFMAs of each column block.
+    auto pv_tile = [&](const uint8_t* kb, const bf16x8 (&pb)[2], auto&& extra) {
+      constexpr int DV = kPvDepth;
+      i16x8 v[DV + 1];
+      auto read_v = [&](int cb) {
+        const uint8_t* p0 = kb + pv_off + 1024 * cb;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0 + 256));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int d = 0; d < DV; ++d) v[d] = read_v(d);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<32>([&](auto cbc) {
+        constexpr int cb = decltype(cbc)::value;
+        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(cb + DV);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, v[cb % (DV + 1)]);
+        OBlock<2 * cb + 0>::mfma(va, pb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        extra(cb);
+        OBlock<2 * cb + 1>::mfma(va, pb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+
+    // ---- online softmax state (base 2, lazy reference) ----
+    // m_ref: reference max per row block (log2 units), the same in the four
+    // lanes of a row; l_part: this lane's share of the running sum.
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    float l_part[2] = {0.f, 0.f};
+    float alpha[2] = {1.f, 1.f};
+    bool any_scale = false;
+    float mx[2], mu[2];
+    bf16x2 pw[2][4];  // P^T operand under construction: K slots 2m, 2m+1
+    float p_even = 0.f;
+
+    // Softmax of one tile of raw scores s (s[2kb + hb][i] = key tb_s + 16kb +
+    // 4grp + i, row block hb), as kSoftmaxSteps short steps so that it can be
+    // spread between MFMAs:
+    //   0-3: mask block (kb, hb)'s keys past the row's limit (only on tiles
+    //        that need it), 4-5: row block max, 6-9: max over the 4 lane
+    //        groups,
+    //   10-11: reference update (a row moves its reference only when its
+    //      maximum grows by more than kRescaleThreshold; the first finite
+    //      maximum needs no rescale because nothing has been accumulated yet),
+    //   12-27: p = 2^(s * scale - mu), running sum, bf16 pairs of P^T (K slot
+    //      j of row block hb is s[2(j/4) + hb][j%4]).
+    auto softmax_step = [&](int step, f32x4(&s)[4], bool need_mask, int tb_s) {
+      if (step < 4) {
+        const int kbk = step >> 1, hb = step & 1;
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tb_s + 16 * kbk + 4 * grp + i;
+            s[2 * kbk + hb][i] = tok < lim[hb] ? s[2 * kbk + hb][i] : -INFINITY;
+          }
+        }
+      } else if (step < 6) {
+        const int hb = step - 4;
+        const f32x4& x0 = s[hb];
+        const f32x4& x1 = s[2 + hb];
+        mx[hb] = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], x1[3]));
+      } else if (step < 10) {
+        const int hb = (step - 6) >> 1;
+        mx[hb] = (step & 1) ? group_max16(mx[hb]) : group_max32(mx[hb]);
+      } else if (step < 12) {
+        {
+          const int hb = step - 10;
+          const float m = mx[hb] * scale_log2;
+          const bool upd = m > m_ref[hb] + kRescaleThreshold;
+          const bool sc = upd && m_ref[hb] != -INFINITY;
+          const float m_new = upd ? m : m_ref[hb];
+          alpha[hb] = sc ? __builtin_amdgcn_exp2f(m_ref[hb] - m_new) : 1.f;
+          l_part[hb] *= alpha[hb];
+          any_scale = any_scale || sc;
+          m_ref[hb] = m_new;
+          mu[hb] = (m_new == -INFINITY) ? 0.f : m_new;
+        }
+      } else if (step < kSoftmaxSteps) {
+        const int j = step - 12;
+        const int hb = j >> 3, jj = j & 7;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * (jj >> 2) + hb][jj & 3], scale_log2, -mu[hb]));
+        l_part[hb] += p;
+        if (jj & 1) {
+          pw[hb][jj >> 1] = bf16x2{(__bf16)p_even, (__bf16)p};
+          asm volatile("" : "+v"(pw[hb][jj >> 1]));  // pack now, not at the end
+        } else {
+          p_even = p;
+        }
+      }
+    };
+    auto pack_p = [&](bf16x8 (&pb)[2]) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        pb[hb] = __builtin_shufflevector(__builtin_shufflevector(pw[hb][0], pw[hb][1], 0, 1, 2, 3),
+                                         __builtin_shufflevector(pw[hb][2], pw[hb][3], 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                         5, 6, 7);
     };
 
     // Tile 0 (and the query rows, loaded before it) have landed once two
@@ -378,24 +588,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     {
       wait_vmem<2 * kLoadsPerWave>();
       asm volatile("" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]), "+v"(q[6]),
-                   "+v"(q[7]), "+v"(q[8]));
-      asm volatile("" : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
-                   "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
-      asm volatile("" : "+v"(q[18]), "+v"(q[19]), "+v"(q[20]), "+v"(q[21]), "+v"(q[22]), "+v"(q[23]),
-                   "+v"(q[24]), "+v"(q[25]), "+v"(q[26]));
-      asm volatile("" : "+v"(q[27]), "+v"(q[28]), "+v"(q[29]), "+v"(q[30]), "+v"(q[31]), "+v"(q[32]),
-                   "+v"(q[33]), "+v"(q[34]), "+v"(q[35]));
-      if (!row_ok) {
-#pragma unroll
-        for (int kk = 0; kk < 36; ++kk) q[kk] = bf16x8{};
-      }
+                   "+v"(q[7]));
+      asm volatile("" : "+v"(q[8]), "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]),
+                   "+v"(q[14]), "+v"(q[15]));
+      asm volatile("" : "+v"(q[16]), "+v"(q[17]), "+v"(q[18]), "+v"(q[19]), "+v"(q[20]), "+v"(q[21]),
+                   "+v"(q[22]), "+v"(q[23]));
+      asm volatile("" : "+v"(q[24]), "+v"(q[25]), "+v"(q[26]), "+v"(q[27]), "+v"(q[28]), "+v"(q[29]),
+                   "+v"(q[30]), "+v"(q[31]));
       __syncthreads();
     }
-    f32x16 s_cur;
-    qk_tile(smem, s_cur, [](int) {});
-
-    float m_ref = -INFINITY;  // running reference max (log2 units), same in lanes l and l^32
-    float l_part = 0.f;       // this lane's share of the running sum
+    o_zero_rec<0>();
+    bf16x8 pb[2];
+    {
+      f32x4 s0[4];
+      qk_tile(smem, s0, [](int) {});
+      const bool nm0 = kv0 + kTile > lim_wave;
+#pragma unroll
+      for (int step = 0; step < kSoftmaxSteps; ++step) softmax_step(step, s0, nm0, kv0);
+      pack_p(pb);
+      any_scale = false;  // nothing accumulated yet
+    }
 
     for (int it = 0; it < ntiles; ++it) {
       const bool has_next = it + 1 < ntiles;
@@ -406,92 +618,48 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       __syncthreads();
 
       const int tb = kv0 + it * kTile;
-      const uint8_t* kb = smem + (it % NSTAGE) * kStageBytes;             // tile it (PV)
-      const uint8_t* kb_next = smem + ((it + 1) % NSTAGE) * kStageBytes;  // tile it+1 (QK^T)
-      const int nt = it + 3;                                              // tile to copy now
-      const int nti = min(nt, last_tile);
-      uint8_t* nbuf = smem + (nt % NSTAGE) * kStageBytes;
-      const TilePages npg = checked(pg_raw);
+      const uint8_t* kb = smem + (it % kStages) * kStageBytes;             // tile it (PV)
+      const uint8_t* kb_next = smem + ((it + 1) % kStages) * kStageBytes;  // tile it+1 (QK^T)
+      const int nt = it + 3;                                               // tile to copy now
+      const int tb_c = kv0 + min(nt, last_tile) * kTile;
+      uint8_t* nbuf = smem + (nt % kStages) * kStageBytes;
+      const TileSrc nsrc = tile_src(tb_c, checked(pg_raw));
       pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile);
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- tile it: mask, scale to log2 units, tile max ----
-      const bool need_mask = tb + kTile > lim;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s_cur[i] * scale_log2;
-        if (need_mask) {
-          const int tok = tb + (i >> 2) * 8 + half * 4 + (i & 3);
-          x = tok < lim ? x : -INFINITY;
+      // ---- QK^T of tile it+1, copies of tile it+3 between its MFMAs ----
+      auto copy_step = [&](int k) {
+        if ((k & 7) == 4 && (k >> 3) < kLoadsPerWave) {
+          static_for<kLoadsPerWave>([&](auto ic) {
+            if (decltype(ic)::value == (k >> 3)) dma(ic, nsrc, nbuf);
+          });
         }
-        s_cur[i] = x;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
-                       fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
-                           fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
-      mx = partner_max(mx);
-
-      // ---- lazy rescale of the running output ----
-      // A row moves its reference only when its maximum grows by more than
-      // kRescaleThreshold; the first finite maximum needs no rescale because
-      // nothing has been accumulated yet.
-      const bool need_update = mx > m_ref + kRescaleThreshold;
-      if (__any(need_update)) {
-        const bool need_scale = need_update && m_ref != -INFINITY;
-        const float m_new = need_update ? mx : m_ref;
-        const float alpha = need_scale ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-        l_part *= alpha;
-        if (__any(need_scale)) o_scale_all(alpha);
-        m_ref = m_new;
-      }
-      const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-      __builtin_amdgcn_sched_barrier(0);
-
-      // ---- QK^T of tile it+1, with P = 2^(x - mu) of tile it (bf16 MFMA B
-      //      operands, 8 keys per 16-key step) and the copies of tile it+3
-      //      issued between its MFMAs ----
-      bf16x8 pb[2];
-      auto softmax_step = [&](int kk) {
-        if (kk < 16) {
-          const float p = __builtin_amdgcn_exp2f(s_cur[kk] - mu);
-          l_part += p;
-          pb[kk >> 3][kk & 7] = (__bf16)p;
-        }
-        if (kk >= 16 && kk < 16 + kLoadsPerWave) dma(kk - 16, kv0 + nti * kTile, npg, nbuf);
       };
-      f32x16 s_next;
+      f32x4 s_next[4];
       if (has_next) {
-        qk_tile(kb_next, s_next, softmax_step);
+        qk_tile(kb_next, s_next, copy_step);
       } else {
-#pragma unroll
-        for (int kk = 0; kk < 36; ++kk) softmax_step(kk);
+        dma_all(nsrc, nbuf);
       }
-      // Materialize the bf16 operands here, not next to the MFMAs.
-      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- O^T += V^T P^T for tile it, V^T read transposed from its stage ----
-      i16x8 v[3];
-      auto read_v = [&](int idx) {
-        const int ks = idx >> 4, cb = idx & 15;
-        const uint8_t* v0p = kb + pv_base[0][cb & 1] + 18432 * ks + 128 * (cb >> 1);
-        const uint8_t* v1p = kb + pv_base[1][cb & 1] + 18432 * ks + 128 * (cb >> 1);
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, v0p));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, v1p));
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      v[0] = read_v(0);
-      v[1] = read_v(1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int idx = 0; idx < 32; ++idx) {
-        if (idx + 2 < 32) v[(idx + 2) % 3] = read_v(idx + 2);
-        const int ks = idx >> 4, cb = idx & 15;
-        o_mfma(cb, __builtin_bit_cast(bf16x8, v[idx % 3]), pb[ks], it == 0 && ks == 0);
-        __builtin_amdgcn_sched_barrier(0);
+      // ---- PV of tile it, softmax of tile it+1 between its MFMAs ----
+      if (has_next) {
+        const bool nm = tb + 2 * kTile > lim_wave;
+        pv_tile(kb, pb, [&](int cb) {
+          if (cb < kSoftmaxSteps) softmax_step(cb, s_next, nm, tb + kTile);
+        });
+        // A row whose reference moved rescales everything accumulated so far
+        // (tiles <= it).
+        if (__any(any_scale)) {
+          o_drain();
+          o_scale_all(alpha[0], alpha[1]);
+        }
+        any_scale = false;
+        pack_p(pb);
+      } else {
+        pv_tile(kb, pb, [](int) {});
       }
-      s_cur = s_next;
     }
 
     // The repeated copies past the end of the piece must land before the next
@@ -500,26 +668,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 
     // ---- epilogue: normalize and store (final output or a workspace partial) ----
     o_drain();
-    const float l_tot = partner_sum(l_part);
-    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    if (bad_len) {
-      inv = NAN;
-      lse_v = NAN;
+    float inv[2], lse_v[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float l_tot = group_sum(l_part[hb]);
+      inv[hb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      lse_v[hb] = l_tot > 0.f ? (m_ref[hb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      if (bad_len) {
+        inv[hb] = NAN;
+        lse_v[hb] = NAN;
+      }
     }
-    if (row_ok) {
-      float* dst;
-      float* dl;
+    float* dst[2];
+    float* dl[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
       if (sg.partial < 0) {
-        dst = out + ((int64_t)b * rows + row) * 512;
-        dl = lse + (int64_t)b * rows + row;
+        dst[hb] = out + ((int64_t)b * rows + row[hb]) * 512;
+        dl[hb] = lse + (int64_t)b * rows + row[hb];
       } else {
         const int64_t slot = (int64_t)sg.partial * nrb + rb;
-        dst = ws_o + (slot * kRowsPerBlock + row_local) * 512;
-        dl = ws_lse + slot * kRowsPerBlock + row_local;
+        dst[hb] = ws_o + (slot * kRowsPerBlock + row_local[hb]) * 512;
+        dl[hb] = ws_lse + slot * kRowsPerBlock + row_local[hb];
       }
-      o_store_rec<0>(dst, half, inv);
-      if (half == 0) *dl = lse_v;
+    }
+    if (row_ok[0]) {
+      o_store_rec<0, 0>(dst[0] + 4 * grp, inv[0]);
+      if (grp == 0) *dl[0] = lse_v[0];
+    }
+    if (row_ok[1]) {
+      o_store_rec<1, 0>(dst[1] + 4 * grp, inv[1]);
+      if (grp == 0) *dl[1] = lse_v[1];
     }
   }
 }
@@ -698,7 +877,7 @@ mla_status check_device(const mla_plan* plan) {
   return MLA_OK;
 }
 
-template <int NSTAGE, bool SINGLE_PAGE>
+template <bool SINGLE_PAGE>
 hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* cache,
                          int64_t num_pages, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
                          float scale_log2, float* out, float* lse, float* ws_o, float* ws_lse,
@@ -707,7 +886,7 @@ hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q
   const char* base = static_cast<const char*>(plan->dev);
   int page_log2 = 0;
   while ((1 << page_log2) < d.page) ++page_log2;
-  hipLaunchKernelGGL((mla::decode_kernel<NSTAGE, SINGLE_PAGE>), dim3(d.grid), dim3(64 * mla::kWaves), 0, stream,
+  hipLaunchKernelGGL((mla::decode_kernel<SINGLE_PAGE>), dim3(d.grid), dim3(64 * mla::kWaves), 0, stream,
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
                      static_cast<const uint8_t*>(cache), num_pages, bt, bt_stride, seq_lens,
                      reinterpret_cast<const int32_t*>(base + plan->off_lens),
@@ -817,9 +996,9 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;
   const bool single = d.page >= d.v.tile_tokens;
   if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile) return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
-  hipError_t e = single ? launch_decode<4, true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
+  hipError_t e = single ? launch_decode<true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
                                                  seq_lens, scale_log2, out, lse, ws_o, ws_lse, st)
-                        : launch_decode<4, false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
+                        : launch_decode<false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
                                                   bt_stride, seq_lens, scale_log2, out, lse, ws_o, ws_lse, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   g_last_error.clear();
