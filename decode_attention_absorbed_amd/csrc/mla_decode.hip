@@ -261,6 +261,37 @@ __device__ __forceinline__ void o_store_rec(float* dst, float inv) {
   }
 }
 
+// Largest |O| over the 32 blocks of row block HB held by this lane.
+template <int HB, int CB>
+__device__ __forceinline__ float o_absmax_rec(float m) {
+  if constexpr (CB < 32) {
+    constexpr int r = 4 * (2 * CB + HB);
+    float a, b;
+    asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(a) : "v"(m), "v"(o_get<r + 0>()), "v"(o_get<r + 1>()));
+    asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(b) : "v"(a), "v"(o_get<r + 2>()), "v"(o_get<r + 3>()));
+    return o_absmax_rec<HB, CB + 1>(b);
+  }
+  return m;
+}
+
+// Store row block HB as a half-precision partial O * c.  Column block pair
+// (cb, cb+1) of a row is 32 consecutive values, lane group g's 8 of them at
+// [8g, 8g+8): block (cb, HB) value i at dst[16cb + i], block (cb+1, HB) value
+// i at dst[16cb + 4 + i] (dst already points at this lane's group), so the
+// four lanes of a row write 64 contiguous bytes per store.
+template <int HB, int CB>
+__device__ __forceinline__ void o_store_half_rec(_Float16* dst, float c) {
+  if constexpr (CB < 32) {
+    constexpr int r0 = 4 * (2 * CB + HB), r1 = 4 * (2 * (CB + 1) + HB);
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    f16x8 w = {(_Float16)(o_get<r0 + 0>() * c), (_Float16)(o_get<r0 + 1>() * c), (_Float16)(o_get<r0 + 2>() * c),
+               (_Float16)(o_get<r0 + 3>() * c), (_Float16)(o_get<r1 + 0>() * c), (_Float16)(o_get<r1 + 1>() * c),
+               (_Float16)(o_get<r1 + 2>() * c), (_Float16)(o_get<r1 + 3>() * c)};
+    *reinterpret_cast<f16x8*>(dst + 16 * CB) = w;
+    o_store_half_rec<HB, CB + 2>(dst, c);
+  }
+}
+
 // Page ids a tile touches (uniform; at most 2 since pages hold >= 16 keys and
 // tiles hold 32).  Out-of-range ids are replaced by page 0 so that a corrupt
 // block table can never make the kernel read outside the cache.
@@ -277,8 +308,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ planned_lens,
     const Segment* __restrict__ segs, const WorkgroupRange* __restrict__ wgs,
     float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse) {
+    float* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
+    float* __restrict__ ws_lse, float* __restrict__ ws_f) {
   // 4 tile stages (144 KB) + the rope part of the query rows (16 KB): the
   // 160 KB of LDS a workgroup may hold.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kWaves * kQpeWaveBytes];
@@ -668,81 +699,138 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 
     // ---- epilogue: normalize and store (final output or a workspace partial) ----
     o_drain();
-    float inv[2], lse_v[2];
+    float l_tot[2], lse_v[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const float l_tot = group_sum(l_part[hb]);
-      inv[hb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      lse_v[hb] = l_tot > 0.f ? (m_ref[hb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-      if (bad_len) {
-        inv[hb] = NAN;
-        lse_v[hb] = NAN;
-      }
+      l_tot[hb] = group_sum(l_part[hb]);
+      lse_v[hb] = l_tot[hb] > 0.f ? (m_ref[hb] + __builtin_amdgcn_logf(l_tot[hb])) * kLn2 : -INFINITY;
+      if (bad_len) lse_v[hb] = NAN;
     }
-    float* dst[2];
-    float* dl[2];
+    if (sg.partial < 0) {
+      // Whole request: out = O / l in fp32.
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      if (sg.partial < 0) {
-        dst[hb] = out + ((int64_t)b * rows + row[hb]) * 512;
-        dl[hb] = lse + (int64_t)b * rows + row[hb];
-      } else {
-        const int64_t slot = (int64_t)sg.partial * nrb + rb;
-        dst[hb] = ws_o + (slot * kRowsPerBlock + row_local[hb]) * 512;
-        dl[hb] = ws_lse + slot * kRowsPerBlock + row_local[hb];
+      for (int hb = 0; hb < 2; ++hb) {
+        float inv = l_tot[hb] > 0.f ? 1.f / l_tot[hb] : 0.f;
+        if (bad_len) inv = NAN;
+        if (!row_ok[hb]) continue;
+        float* dst = out + ((int64_t)b * rows + row[hb]) * 512 + 4 * grp;
+        if (hb == 0)
+          o_store_rec<0, 0>(dst, inv);
+        else
+          o_store_rec<1, 0>(dst, inv);
+        if (grp == 0) lse[(int64_t)b * rows + row[hb]] = lse_v[hb];
       }
-    }
-    if (row_ok[0]) {
-      o_store_rec<0, 0>(dst[0] + 4 * grp, inv[0]);
-      if (grp == 0) *dl[0] = lse_v[0];
-    }
-    if (row_ok[1]) {
-      o_store_rec<1, 0>(dst[1] + 4 * grp, inv[1]);
-      if (grp == 0) *dl[1] = lse_v[1];
+    } else {
+      // Piece of a split request: the partial o = O / l is stored as O * 2^(15-e)
+      // in fp16, e the binary exponent of the row's largest |O| (so every
+      // stored value is below 2^15 in magnitude and keeps 11 bits), with
+      // f = 2^(e-15) / l and lse beside it: o = stored * f.  Within a row,
+      // position 32 (cb / 2) + 8 grp + 4 (cb % 2) + i holds column
+      // 16 cb + 4 grp + i.
+      const int64_t slot = (int64_t)sg.partial * nrb + rb;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float amax = hb == 0 ? o_absmax_rec<0, 0>(0.f) : o_absmax_rec<1, 0>(0.f);
+        amax = group_max16(group_max32(amax));
+        const int e = max(__builtin_amdgcn_frexp_expf(amax), -110);
+        const float c = __builtin_ldexpf(1.f, 15 - e);
+        float f = l_tot[hb] > 0.f ? __builtin_ldexpf(1.f / l_tot[hb], e - 15) : 0.f;
+        if (bad_len) f = NAN;
+        if (!row_ok[hb]) continue;
+        const int64_t ri = slot * kRowsPerBlock + row_local[hb];
+        _Float16* dst = reinterpret_cast<_Float16*>(ws_o) + ri * 512 + 8 * grp;
+        if (hb == 0)
+          o_store_half_rec<0, 0>(dst, c);
+        else
+          o_store_half_rec<1, 0>(dst, c);
+        if (grp == 0) {
+          ws_lse[ri] = lse_v[hb];
+          ws_f[ri] = f;
+        }
+      }
     }
   }
 }
 
-// One workgroup = 2 rows x 512 columns of one split request; each thread owns
-// 4 columns of one row and walks that request's partials.
+// One workgroup = one row of one split request.  Stored position 8l + e of a
+// row (lane l) holds column 32(l/4) + 4(l%4) + e for e < 4 and
+// 32(l/4) + 16 + 4(l%4) + e - 4 otherwise.  All waves derive
+// lse = logsumexp_s lse_s for the row; the partial weights
+// exp(lse_s - lse) f_s go to LDS in chunks of kCombineChunk; wave j (0..3)
+// then sums the partials s = j, j+4, ... of the chunk, and the four waves'
+// sums meet in LDS.
+constexpr int kCombineChunk = 256;
 __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restrict__ jobs,
-                                                       const float* __restrict__ ws_o,
-                                                       const float* __restrict__ ws_lse, int32_t rows,
-                                                       int32_t rpb, int32_t nrb, float* __restrict__ out,
+                                                       const uint16_t* __restrict__ ws_o,
+                                                       const float* __restrict__ ws_lse,
+                                                       const float* __restrict__ ws_f, int32_t rows, int32_t rpb,
+                                                       int32_t nrb, float* __restrict__ out,
                                                        float* __restrict__ lse) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  __shared__ float wts[kCombineChunk];
+  __shared__ f32x4 red[3][64][2];
   const CombineJob job = jobs[blockIdx.x];
-  const int row = blockIdx.y * 2 + (threadIdx.x >> 7);
-  if (row >= rows) return;
-  const int c = (threadIdx.x & 127) * 4;
+  const int row = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int rb = row / rpb, rl = row - rb * rpb;
-  auto slot_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
+  auto ri_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
 
   float m = -INFINITY;
   bool any_nan = false;  // fmaxf drops NaN; a NaN partial (length mismatch) must stay loud
-  for (int s = 0; s < job.n; ++s) {
-    const float v = ws_lse[slot_of(s)];
-    any_nan |= (v != v);
-    m = fmaxf(m, v);
+  for (int s = lane; s < job.n; s += 64) {
+    const float x = ws_lse[ri_of(s)];
+    any_nan |= (x != x);
+    m = fmaxf(m, x);
   }
-  float lse_v = -INFINITY;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (any_nan) {
-    lse_v = NAN;
-    acc = f32x4{NAN, NAN, NAN, NAN};
-  } else if (m != -INFINITY) {
-    float z = 0.f;
-    for (int s = 0; s < job.n; ++s) z += __expf(ws_lse[slot_of(s)] - m);
-    lse_v = m + __logf(z);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  any_nan = __any(any_nan);
+  float z = 0.f;
+  if (m != -INFINITY)
+    for (int s = lane; s < job.n; s += 64) z += __expf(ws_lse[ri_of(s)] - m);
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+  const float lse_v = any_nan ? NAN : (m == -INFINITY ? -INFINITY : m + __logf(z));
+  const bool live = !any_nan && m != -INFINITY;
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    for (int c0 = 0; c0 < job.n; c0 += kCombineChunk) {
+      const int cn = min(kCombineChunk, job.n - c0);
+      if (threadIdx.x < cn) {
+        const int64_t ri = ri_of(c0 + threadIdx.x);
+        wts[threadIdx.x] = __expf(ws_lse[ri] - lse_v) * ws_f[ri];
+      }
+      __syncthreads();
 #pragma unroll 4
-    for (int s = 0; s < job.n; ++s) {
-      const int64_t sl = slot_of(s);
-      const float w = __expf(ws_lse[sl] - lse_v);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + sl * 512 + c);
-      acc += w * v;
+      for (int k = wv; k < cn; k += 4) {
+        const float w = wts[k];
+        const f16x8 v = *reinterpret_cast<const f16x8*>(ws_o + ri_of(c0 + k) * 512 + 8 * lane);
+        acc0 += w * f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        acc1 += w * f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+      }
+      __syncthreads();
     }
   }
-  *reinterpret_cast<f32x4*>(out + ((int64_t)job.b * rows + row) * 512 + c) = acc;
-  if (c == 0) lse[(int64_t)job.b * rows + row] = lse_v;
+  if (wv > 0) {
+    red[wv - 1][lane][0] = acc0;
+    red[wv - 1][lane][1] = acc1;
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      acc0 += red[j][lane][0];
+      acc1 += red[j][lane][1];
+    }
+    if (any_nan) {
+      acc0 = f32x4{NAN, NAN, NAN, NAN};
+      acc1 = acc0;
+    }
+    float* dst = out + ((int64_t)job.b * rows + row) * 512 + 32 * (lane >> 2) + 4 * (lane & 3);
+    *reinterpret_cast<f32x4*>(dst) = acc0;
+    *reinterpret_cast<f32x4*>(dst + 16) = acc1;
+    if (lane == 0) lse[(int64_t)job.b * rows + row] = lse_v;
+  }
 }
 
 }  // namespace
@@ -845,13 +933,17 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Workspace checks shared by the entry points; splits it into the partial
-// outputs and the partial lse arrays.
-mla_status check_workspace(const mla_plan* plan, void* workspace, size_t workspace_bytes, float** ws_o,
-                           float** ws_lse) {
+// outputs (fp16), the partial lse and the partial scale factors.
+struct Workspace {
+  uint16_t* o = nullptr;
+  float* lse = nullptr;
+  float* f = nullptr;
+};
+
+mla_status check_workspace(const mla_plan* plan, void* workspace, size_t workspace_bytes, Workspace* ws) {
   const mla::PlanData& d = plan->d;
   const size_t need = mla::workspace_bytes(d);
-  *ws_o = nullptr;
-  *ws_lse = nullptr;
+  *ws = Workspace{};
   if (need == 0) return MLA_OK;
   if (!workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL but the plan needs " + std::to_string(need) + " bytes");
@@ -859,10 +951,11 @@ mla_status check_workspace(const mla_plan* plan, void* workspace, size_t workspa
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace has " + std::to_string(workspace_bytes) + " bytes, the plan needs " + std::to_string(need));
   if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  const size_t slots = (size_t)d.num_partials * d.nrb;
-  const size_t o_bytes = align256(slots * d.v.rows_per_block() * 512 * sizeof(float));
-  *ws_o = static_cast<float*>(workspace);
-  *ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  const mla::WorkspaceLayout lay = mla::workspace_layout(d);
+  char* base = static_cast<char*>(workspace);
+  ws->o = reinterpret_cast<uint16_t*>(base + lay.off_o);
+  ws->lse = reinterpret_cast<float*>(base + lay.off_lse);
+  ws->f = reinterpret_cast<float*>(base + lay.off_f);
   return MLA_OK;
 }
 
@@ -880,8 +973,7 @@ mla_status check_device(const mla_plan* plan) {
 template <bool SINGLE_PAGE>
 hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* cache,
                          int64_t num_pages, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
-                         float scale_log2, float* out, float* lse, float* ws_o, float* ws_lse,
-                         hipStream_t stream) {
+                         float scale_log2, float* out, float* lse, const Workspace& ws, hipStream_t stream) {
   const mla::PlanData& d = plan->d;
   const char* base = static_cast<const char*>(plan->dev);
   int page_log2 = 0;
@@ -892,7 +984,7 @@ hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q
                      reinterpret_cast<const int32_t*>(base + plan->off_lens),
                      reinterpret_cast<const mla::Segment*>(base + plan->off_segs),
                      reinterpret_cast<const mla::WorkgroupRange*>(base + plan->off_wgs), scale_log2, d.rows,
-                     d.heads, d.q_len, page_log2, d.nrb, out, lse, ws_o, ws_lse);
+                     d.heads, d.q_len, page_log2, d.nrb, out, lse, ws.o, ws.lse, ws.f);
   return hipGetLastError();
 }
 
@@ -985,9 +1077,8 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
                                               std::to_string(d.max_pages) + ")");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-  float* ws_o = nullptr;
-  float* ws_lse = nullptr;
-  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws_o, &ws_lse);
+  Workspace ws;
+  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws);
   if (st_ws != MLA_OK) return st_ws;
   mla_status st_dev = check_device(plan);
   if (st_dev != MLA_OK) return st_dev;
@@ -997,9 +1088,9 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
   const bool single = d.page >= d.v.tile_tokens;
   if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile) return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
   hipError_t e = single ? launch_decode<true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
-                                                 seq_lens, scale_log2, out, lse, ws_o, ws_lse, st)
+                                                 seq_lens, scale_log2, out, lse, ws, st)
                         : launch_decode<false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
-                                                  bt_stride, seq_lens, scale_log2, out, lse, ws_o, ws_lse, st);
+                                                  bt_stride, seq_lens, scale_log2, out, lse, ws, st);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   g_last_error.clear();
   return MLA_OK;
@@ -1010,18 +1101,17 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!out || !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
   if (!aligned(out, 16) || !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
-  float* ws_o = nullptr;
-  float* ws_lse = nullptr;
-  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws_o, &ws_lse);
+  Workspace ws;
+  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws);
   if (st_ws != MLA_OK) return st_ws;
   mla_status st_dev = check_device(plan);
   if (st_dev != MLA_OK) return st_dev;
   const mla::PlanData& d = plan->d;
   if (!d.jobs.empty()) {
     const char* base = static_cast<const char*>(plan->dev);
-    hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)((d.rows + 1) / 2)), dim3(256),
-                       0, static_cast<hipStream_t>(stream),
-                       reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs), ws_o, ws_lse, d.rows,
+    hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)d.rows), dim3(256), 0,
+                       static_cast<hipStream_t>(stream),
+                       reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs), ws.o, ws.lse, ws.f, d.rows,
                        d.v.rows_per_block(), d.nrb, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

@@ -217,14 +217,21 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
   return kOk;
 }
 
-size_t workspace_bytes(const PlanData& p) {
-  // fp32 partial outputs [slots][rows_per_block][512], then lse [slots][rows_per_block]
+WorkspaceLayout workspace_layout(const PlanData& p) {
+  // fp16 partial outputs [slots][rows_per_block][512], then lse and scale
+  // factors [slots][rows_per_block] in fp32, each part 256-byte aligned.
   const size_t slots = (size_t)p.num_partials * p.nrb;
   const size_t rpb = (size_t)p.v.rows_per_block();
-  const size_t o = slots * rpb * 512 * sizeof(float);
-  const size_t l = slots * rpb * sizeof(float);
-  if (slots == 0) return 0;
-  return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  WorkspaceLayout w;
+  if (slots == 0) return w;
+  w.off_o = 0;
+  w.off_lse = al(slots * rpb * 512 * 2);
+  w.off_f = w.off_lse + al(slots * rpb * 4);
+  w.total = w.off_f + al(slots * rpb * 4);
+  return w;
 }
+
+size_t workspace_bytes(const PlanData& p) { return workspace_layout(p).total; }
 
 }  // namespace mla

@@ -65,6 +65,11 @@ struct PlanTuning {
 int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads, int32_t page,
                int32_t num_cus, const PlanTuning& tuning, PlanData* out, std::string* err);
 
+// Byte offsets of the workspace parts (all zero when no request is split).
+struct WorkspaceLayout {
+  size_t off_o = 0, off_lse = 0, off_f = 0, total = 0;
+};
+WorkspaceLayout workspace_layout(const PlanData& p);
 size_t workspace_bytes(const PlanData& p);
 
 }  // namespace mla

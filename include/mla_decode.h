@@ -90,8 +90,9 @@ mla_status mla_decode_plan_host(const int32_t* seq_lens_host, int32_t batch, int
                                 mla_plan** plan_out);
 
 /* Bytes of device workspace mla_decode needs with this plan (0 if no request
- * is split).  The workspace holds one fp32 partial (rows x 512 values plus a
- * log-sum-exp per row) per piece of every split request. */
+ * is split).  The workspace holds one partial per piece of every split
+ * request: rows x 512 values in fp16 (scaled per row so that no value
+ * overflows), plus a log-sum-exp and a scale factor per row in fp32. */
 size_t mla_decode_workspace_bytes(const mla_plan* plan);
 
 /*

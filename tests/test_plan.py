@@ -43,7 +43,7 @@ def check_plan(lens, q_len, heads, page, num_cus):
     assert busy <= max(nrb, num_cus * (2 if rpb == 64 else 1))
     # workspace size
     slots = p.query(bnd.MLA_Q_NUM_PARTIALS) * nrb
-    expect = 0 if slots == 0 else (-(-slots * rpb * 512 * 4 // 256) * 256 + -(-slots * rpb * 4 // 256) * 256)
+    expect = 0 if slots == 0 else (-(-slots * rpb * 512 * 2 // 256) * 256 + 2 * (-(-slots * rpb * 4 // 256) * 256))
     assert p.workspace_bytes == expect
     return p, seg, wg, T
 
