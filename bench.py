@@ -12,6 +12,11 @@ larger than 1 GB).
 Prints ONE JSON line (value = algorithmic TFLOP/s of the whole step).
 
     python bench.py [--config dsv3] [--steps 50] [--warmup 10]
+
+HBM traffic evidence (roofline.traffic): rocprofv3 counter passes over this
+script, one counter per pass, for the decode workload and for a plain device
+copy of known size (--calibrate-copy), turned into profiles/traffic_<config>.json
+by --traffic-from; the commands are listed in profiles/traffic_<config>.md.
 """
 from __future__ import annotations
 
@@ -48,6 +53,78 @@ def load_traffic(config: str, per_launch_bytes_alg: int):
     if t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("decode_bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written per launch
+COPY_LAUNCHES = 5
+
+
+def calibrate_copy() -> int:
+    """Plain device-to-device copies of COPY_BYTES, the counters' yardstick."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(COPY_LAUNCHES):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": COPY_LAUNCHES}), flush=True)
+    return 0
+
+
+def _counter_per_dispatch(directory: str, counter: str, kernel_part: str) -> list:
+    """Per-dispatch values (KiB) of one counter for kernels whose name contains kernel_part."""
+    import csv
+
+    vals = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_part in r["Kernel_Name"]:
+                key = (r.get("Agent_Id"), r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=lambda k: int(k[1]))]
+
+
+def traffic_from(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> int:
+    """Turns the four counter passes into profiles/traffic_<config>.json."""
+    import statistics
+
+    def med(xs):
+        if not xs:
+            raise SystemExit("no counter rows found")
+        return statistics.median(xs)
+
+    # the copy kernel is the only kernel in the calibration run besides torch's fill
+    cf = [v for v in _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "") if v > 0]
+    cw = [v for v in _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "") if v > 0]
+    cf_k, cw_k = max(cf), max(cw)
+    f_fetch = COPY_BYTES / (cf_k * 1024.0)
+    f_write = COPY_BYTES / (cw_k * 1024.0)
+    fetch = med(_counter_per_dispatch(fetch_dir, "FETCH_SIZE", "decode_kernel"))
+    write = med(_counter_per_dispatch(write_dir, "WRITE_SIZE", "decode_kernel"))
+    cfetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "combine_kernel")
+    cwrite = _counter_per_dispatch(write_dir, "WRITE_SIZE", "combine_kernel")
+    res = {
+        "config": config,
+        "kernel_sha": kernel_sha(),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": cf_k,
+        "copy_write_kib": cw_k,
+        "fetch_factor": f_fetch,
+        "write_factor": f_write,
+        "decode_fetch_kib": fetch,
+        "decode_write_kib": write,
+        "decode_bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write,
+        "combine_bytes_per_launch": (med(cfetch) * 1024.0 * f_fetch + med(cwrite) * 1024.0 * f_write)
+        if cfetch and cwrite else None,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    with open(path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def cpu_baseline(x, seconds: float) -> dict:
@@ -148,15 +225,26 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
     cmb_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
     dec_avg = sum(dec_ms) / steps
     cmb_avg = sum(cmb_ms) / steps
+    # Kernel duration for the roofline: the same decode launches back to back
+    # between one pair of events on the launch stream (the per-kernel events
+    # above also hold the gap between the previous kernel's end and this start).
+    burst = max(steps, 20)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(burst):
+        partials(i)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    dec_burst = b0.elapsed_time(b1) / burst
 
     flops = roof["flops"]
     nbytes = roof["bytes"]
     bound = roof["bound"]
     if bound == "hbm":
-        achieved = nbytes / (dec_avg * 1e-3) / 1e9
+        achieved = nbytes / (dec_burst * 1e-3) / 1e9
         peak, unit = acc.PEAK_HBM_BYTES_PER_S / 1e9, "GB/s"
     else:
-        achieved = flops / (dec_avg * 1e-3) / 1e12
+        achieved = flops / (dec_burst * 1e-3) / 1e12
         peak, unit = acc.PEAK_BF16_FLOPS / 1e12, "TFLOP/s"
     traffic = load_traffic(config, nbytes)
     res = {
@@ -190,9 +278,11 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
             "frac": achieved / peak,
             "traffic": traffic,
             "kernel": "decode_kernel",
+            "duration_ms": dec_burst,
         },
         "step_roofline_frac": roof["t_bound"] / (ms_step * 1e-3),
-        "decode_kernel_ms": dec_avg,
+        "decode_kernel_ms": dec_burst,
+        "decode_kernel_ms_in_step": dec_avg,
         "decode_kernel_ms_p10_p90": [dec_ms[steps // 10], dec_ms[(9 * steps) // 10]],
         "combine_kernel_ms": cmb_avg,
         "plan_ms": plan_ms,
@@ -220,7 +310,14 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true", help="run the plain copy the traffic counters are scaled by")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<config>.json from rocprofv3 counter output (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_from(args.config, *args.traffic_from)
+    if args.calibrate_copy:
+        return calibrate_copy()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by request; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
