@@ -181,14 +181,15 @@ __device__ __forceinline__ bf16x8 load16(const void* src) {
 // asm are handled here: the first step takes srcC = 0 (no VALU write of the
 // accumulator right before an MFMA reads it; early clobber so the result does
 // not share registers with an operand), and s_mfma_drain waits out the
-// XDL-write -> VALU-read latency before anything reads the results.  Every
-// MFMA issued as asm starts with s_nop 1: a VALU write of a source register
-// needs two wait states before an MFMA reads it.
+// XDL-write -> VALU-read latency before anything reads the results.  No MFMA
+// operand is written by VALU right before the MFMA (two wait states are
+// needed); the operands come from LDS, global loads or much earlier VALU
+// work, and the build's assembly is checked for the hazard.
 __device__ __forceinline__ void s_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b, bool first) {
   if (first)
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ void s_mfma_drain(f32x4 (&acc)[4]) {

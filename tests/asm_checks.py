@@ -1,0 +1,111 @@
+"""Checks on the gfx950 assembly of the decode kernel (test infrastructure).
+
+The decode kernel issues its MFMAs, query loads and LDS copies as inline asm,
+which the compiler neither schedules around nor protects with wait states or
+wait counts.  These checks read the compiled assembly and verify what the
+kernel's comments promise:
+  * no VALU instruction writes an MFMA operand (or result register) less than
+    two wait states before the MFMA;
+  * the registers of the asynchronous query loads are not touched between the
+    load and the first explicit vmcnt wait after it;
+  * every vmcnt wait in the decode kernel is one the source writes explicitly
+    (the compiler adds none: an extra one would serialize the copy pipeline).
+"""
+from __future__ import annotations
+
+import re
+
+DECODE_PREFIX = "_ZN3mla12_GLOBAL__N_113decode_kernel"
+
+
+def _regs(tok: str) -> set:
+    tok = tok.strip().rstrip(",")
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _split(line: str):
+    t = line.split(";")[0].strip()
+    parts = t.split(None, 1)
+    if not parts:
+        return "", []
+    if len(parts) == 1:
+        return parts[0], []
+    return parts[0], [o.strip() for o in parts[1].split(",")]
+
+
+def kernel_bodies(asm: str, prefix: str = DECODE_PREFIX) -> list:
+    """Instruction lines of every function whose symbol starts with prefix."""
+    lines = asm.split("\n")
+    out = []
+    for i, l in enumerate(lines):
+        if l.startswith(prefix) and l.split(";")[0].rstrip().endswith(":"):
+            body = []
+            for t in lines[i + 1 :]:
+                if "s_endpgm" in t:
+                    break
+                t = t.strip()
+                if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
+                    continue
+                body.append(t)
+            out.append(body)
+    return out
+
+
+def mfma_hazards(body: list) -> list:
+    """(valu, mfma) pairs closer than two wait states (linear scan)."""
+    bad = []
+    for i, t in enumerate(body):
+        op, ops = _split(t)
+        if not op.startswith("v_mfma"):
+            continue
+        touched = set()
+        for o in ops:
+            touched |= _regs(o)
+        need, j = 2, i - 1
+        while need > 0 and j >= 0:
+            pop, pops = _split(body[j])
+            if pop == "s_nop":
+                need -= int(pops[0], 0) + 1
+                j -= 1
+                continue
+            if pop.startswith("v_") and not pop.startswith(("v_mfma", "v_readlane", "v_readfirstlane", "v_cmp")):
+                written = _regs(pops[0]) if pops else set()
+                if pop.startswith("v_permlane"):
+                    for o in pops[:2]:
+                        written |= _regs(o)
+                if written & touched:
+                    bad.append((body[j], t))
+                    break
+            need -= 1
+            j -= 1
+    return bad
+
+
+def async_load_violations(body: list) -> list:
+    """Instructions that touch an asm query load's registers before the next vmcnt wait."""
+    bad = []
+    for i, t in enumerate(body):
+        op, ops = _split(t)
+        if op != "global_load_dwordx4" or len(ops) < 2 or ops[-1] != "off":
+            continue
+        dst = _regs(ops[0])
+        for u in body[i + 1 :]:
+            if re.match(r"s_waitcnt\b.*vmcnt", u):
+                break
+            uop, uops = _split(u)
+            if uop.startswith("global_load"):
+                continue
+            if any(_regs(o) & dst for o in uops):
+                bad.append((t, u))
+                break
+    return bad
+
+
+def vmcnt_waits(body: list) -> list:
+    return [t for t in body if re.match(r"s_waitcnt\b", t) and "vmcnt" in t]

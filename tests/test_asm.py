@@ -1,0 +1,55 @@
+"""Compiles the decode kernel for gfx950 (no GPU needed) and checks its assembly."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from tests import asm_checks
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "decode_attention_absorbed_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc):
+        hipcc = shutil.which("hipcc")
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    from decode_attention_absorbed_amd.build import HIP_FLAGS
+
+    out = str(tmp_path_factory.mktemp("asm") / "mla_decode.s")
+    flags = [f for f in HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "mla_decode.hip"), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read()
+
+
+def test_decode_kernels_present(asm):
+    bodies = asm_checks.kernel_bodies(asm)
+    assert len(bodies) == 2  # one page per tile / two pages per tile
+    for b in bodies:
+        assert sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in b) >= 136
+
+
+def test_no_valu_to_mfma_hazards(asm):
+    for body in asm_checks.kernel_bodies(asm):
+        assert asm_checks.mfma_hazards(body) == []
+
+
+def test_async_query_loads_untouched_until_waited(asm):
+    for body in asm_checks.kernel_bodies(asm):
+        assert sum(t.startswith("global_load_dwordx4") for t in body) == 32
+        assert asm_checks.async_load_violations(body) == []
+
+
+def test_only_explicit_vmcnt_waits(asm):
+    # 18 = two tiles of copies in flight (prologue), 9 = one tile (loop), 0 = drain
+    for body in asm_checks.kernel_bodies(asm):
+        waits = asm_checks.vmcnt_waits(body)
+        counts = sorted({int(w.split("vmcnt(")[1].split(")")[0]) for w in waits})
+        assert counts == [0, 9, 18], waits
