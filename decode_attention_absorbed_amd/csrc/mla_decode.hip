@@ -86,6 +86,7 @@ constexpr int kQkDepth = MLA_QK_DEPTH;  // K steps of LDS reads in flight ahead 
 constexpr int kPvDepth = MLA_PV_DEPTH;  // column blocks of V^T reads in flight ahead of the PV MFMAs
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kMuFloor = -1e30f;         // subtracted reference of a row with no visible key yet
 static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of copies");
 
 // LDS layout of a 32-key tile (36 KB), column major: the 16-byte chunk c
@@ -111,12 +112,12 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 
 __device__ __forceinline__ float group_max32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float group_max16(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return max3(__uint_as_float(s[0]), __uint_as_float(s[1]), __uint_as_float(s[1]));
 }
 
 __device__ __forceinline__ float group_sum(float x) {
@@ -382,12 +383,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
 
     // Block-table entries of a tile (scalar loads, checked when used).
+    // The piece's first 64 block-table entries sit in one register, lane i
+    // holding page first_pg + i, loaded once per piece; the tile loop reads
+    // them with readlane, so no memory load (and no wait on one) sits between
+    // the LDS reads of the loop.  Pages beyond the first 64 of a piece come
+    // from scalar loads.
+    const int first_pg = kv0 >> page_log2;
+    const int npg_piece = ((kv1 - 1) >> page_log2) - first_pg + 1;
+    const int pg_lane = lane < npg_piece ? bt_row[first_pg + lane] : 0;
+    auto page_at = [&](int pidx) {
+      const int rel = pidx - first_pg;
+      return rel < 64 ? __builtin_amdgcn_readlane(pg_lane, rel) : bt_row[pidx];
+    };
     auto fetch_pages = [&](int tb) {
       TilePages tp;
       tp.first = tb >> page_log2;
       const int last = (min(tb + kTile, kv1) - 1) >> page_log2;
-      tp.pg[0] = bt_row[tp.first];
-      tp.pg[1] = SINGLE_PAGE ? tp.pg[0] : bt_row[min(tp.first + 1, last)];
+      tp.pg[0] = page_at(tp.first);
+      tp.pg[1] = SINGLE_PAGE ? tp.pg[0] : page_at(min(tp.first + 1, last));
       return tp;
     };
     auto checked = [&](TilePages tp) {
@@ -438,11 +451,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // tiles of this one land in LDS.
     __syncthreads();
 
+    const int last_tile = ntiles - 1;
+    // Tile 0 first, then the queries, then tiles 1 and 2: the first wait
+    // (two tiles still in flight) covers tile 0 and the queries.
+    dma_all(tile_src(kv0, checked(fetch_pages(kv0))), smem);
+
     // Query rows as the B operand: q[16hb + ks] holds dims 32ks + 8grp .. +7
     // of row hb (c_kv part, registers); the rope part is copied to this
     // wave's LDS slice (4 copies of 1 KB: slot p = row p/8, chunk p%8).  Rows
     // past the end load row 0: their scores are masked and they are never
-    // stored.  Issued first so that the wait for tile 0 also covers them.
+    // stored.
     bf16x8 q[2 * kNopeSteps];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -471,9 +489,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // iteration issues exactly one tile of copies (past the end of the piece
     // it repeats the last tile into a stage nobody reads), so every wait below
     // has a fixed count.
-    const int last_tile = ntiles - 1;
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
+    for (int st = 1; st < 3; ++st) {
       const int ti = min(st, last_tile);
       const int tb_c = kv0 + ti * kTile;
       dma_all(tile_src(tb_c, checked(fetch_pages(tb_c))), smem + st * kStageBytes);
@@ -546,7 +563,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     float l_part[2] = {0.f, 0.f};
     float alpha[2] = {1.f, 1.f};
     bool any_scale = false;
-    float mx[2], mu[2];
+    float mx[2], mu[2] = {kMuFloor, kMuFloor};
     bf16x2 pw[2][4];  // P^T operand under construction: K slots 2m, 2m+1
     float p_even = 0.f;
 
@@ -564,7 +581,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     auto softmax_step = [&](int step, f32x4(&s)[4], bool need_mask, int tb_s) {
       if (step < 4) {
         const int kbk = step >> 1, hb = step & 1;
-        if (need_mask) {
+        if (__builtin_amdgcn_readfirstlane((int)need_mask)) {  // uniform: branch, not an exec mask
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = tb_s + 16 * kbk + 4 * grp + i;
@@ -581,16 +598,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
         mx[hb] = (step & 1) ? group_max16(mx[hb]) : group_max32(mx[hb]);
       } else if (step < 12) {
         {
+          // mu = max(m_ref, kMuFloor) is the reference actually subtracted,
+          // so alpha = 2^(mu_old - mu_new) needs no case for -inf: it is 1
+          // without an update and 0 for a row's first finite maximum (when
+          // nothing has been accumulated for that row).
           const int hb = step - 10;
           const float m = mx[hb] * scale_log2;
           const bool upd = m > m_ref[hb] + kRescaleThreshold;
-          const bool sc = upd && m_ref[hb] != -INFINITY;
           const float m_new = upd ? m : m_ref[hb];
-          alpha[hb] = sc ? __builtin_amdgcn_exp2f(m_ref[hb] - m_new) : 1.f;
+          const float mu_new = fmaxf(m_new, kMuFloor);
+          alpha[hb] = __builtin_amdgcn_exp2f(mu[hb] - mu_new);
           l_part[hb] *= alpha[hb];
-          any_scale = any_scale || sc;
+          any_scale = any_scale || (upd && mu[hb] > kMuFloor);
           m_ref[hb] = m_new;
-          mu[hb] = (m_new == -INFINITY) ? 0.f : m_new;
+          mu[hb] = mu_new;
         }
       } else if (step < kSoftmaxSteps) {
         const int j = step - 12;
@@ -613,8 +634,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
                                          5, 6, 7);
     };
 
-    // Tile 0 (and the query rows, loaded before it) have landed once two
-    // tiles of copies are still in flight.  The empty asm statements tie the
+    // Tile 0 and the query rows (issued before tiles 1 and 2) have landed
+    // once two tiles of copies are still in flight.  The empty asm statements tie the
     // query registers to this point: the loads fill them asynchronously, so
     // nothing may read, copy or reuse them before the wait.
     {
@@ -656,7 +677,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       const int tb_c = kv0 + min(nt, last_tile) * kTile;
       uint8_t* nbuf = smem + (nt % kStages) * kStageBytes;
       const TileSrc nsrc = tile_src(tb_c, checked(pg_raw));
-      pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- QK^T of tile it+1, copies of tile it+3 between its MFMAs ----
@@ -692,6 +712,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       } else {
         pv_tile(kb, pb, [](int) {});
       }
+      // Pages of the tile the next iteration copies.  Looked up here, after
+      // the last LDS read of the iteration: a scalar load in flight would make
+      // every LDS wait until it lands a full wait.
+      pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile);
     }
 
     // The repeated copies past the end of the piece must land before the next
