@@ -77,10 +77,10 @@ constexpr int kQSteps = 576 / 32;                      // 18 K steps of QK^T
 constexpr int kNopeSteps = 512 / 32;                   // the first 16 come from c_kv
 constexpr int kQpeWaveBytes = 32 * 64 * 2;             // q_pe of one wave's 32 rows in LDS
 #ifndef MLA_QK_DEPTH
-#define MLA_QK_DEPTH 2
+#define MLA_QK_DEPTH 1
 #endif
 #ifndef MLA_PV_DEPTH
-#define MLA_PV_DEPTH 3
+#define MLA_PV_DEPTH 2
 #endif
 constexpr int kQkDepth = MLA_QK_DEPTH;  // K steps of LDS reads in flight ahead of the QK^T MFMAs
 constexpr int kPvDepth = MLA_PV_DEPTH;  // column blocks of V^T reads in flight ahead of the PV MFMAs
@@ -88,6 +88,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kMuFloor = -1e30f;         // subtracted reference of a row with no visible key yet
 static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of copies");
+static_assert(kLoadsPerWave - 5 + kSoftmaxSteps == 32, "PV gaps: 4 copies, then the softmax steps");
 
 // LDS layout of a 32-key tile (36 KB), column major: the 16-byte chunk c
 // (0..71) of key row t (0..31) sits at slot 32c + (t ^ 8(c & 1)).
@@ -499,8 +500,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 
     // QK^T of one tile: acc[2kb + hb] = S^T block (keys 16kb.., rows 16hb..).
     // `extra(k)` (k = 4ks + j) is called between the MFMAs so that
-    // independent work issues while the matrix pipe runs.
-    auto qk_tile = [&](const uint8_t* kb, f32x4(&acc)[4], auto&& extra) {
+    // independent work issues while the matrix pipe runs; `tail()` before
+    // the MFMAs of the last step (the next phase's first LDS reads).  With
+    // `drain`, the results are readable by VALU on return; without, the
+    // caller keeps >= 19 instructions between the last MFMA and any VALU
+    // access of acc (checked on the assembly).
+    auto qk_tile = [&](const uint8_t* kb, f32x4(&acc)[4], auto&& extra, auto&& tail, bool drain) {
       constexpr int D = kQkDepth;
       bf16x8 a[D + 1][2];
       bf16x8 qb[2][2];  // rope steps: [e][hb]
@@ -519,6 +524,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ++ks) {
         if (ks + D < kQSteps) read_step(ks + D);
+        if (ks == kQSteps - 1) {
+          tail();
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           extra(4 * ks + j);
@@ -527,26 +536,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      s_mfma_drain(acc);
+      if (drain) s_mfma_drain(acc);
     };
 
-    // O^T += V^T P^T for one tile, V^T read transposed from its stage;
-    // `extra(cb)` is called between the two MFMAs of each column block.
-    auto pv_tile = [&](const uint8_t* kb, const bf16x8 (&pb)[2], auto&& extra) {
-      constexpr int DV = kPvDepth;
-      i16x8 v[DV + 1];
-      auto read_v = [&](int cb) {
-        const uint8_t* p0 = kb + pv_off + 1024 * cb;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0 + 256));
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
+    // O^T += V^T P^T for one tile, V^T read transposed from its stage.
+    // pv_prefetch issues the reads of the first kPvDepth column blocks (it may
+    // run inside the previous phase); pv_run does the 32 column blocks and
+    // calls `extra(cb)` between the two MFMAs of each.
+    constexpr int DV = kPvDepth;
+    auto read_v = [&](const uint8_t* kb, int cb) {
+      const uint8_t* p0 = kb + pv_off + 1024 * cb;
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0 + 256));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto pv_prefetch = [&](const uint8_t* kb, i16x8 (&v)[DV + 1]) {
 #pragma unroll
-      for (int d = 0; d < DV; ++d) v[d] = read_v(d);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < DV; ++d) v[d] = read_v(kb, d);
+    };
+    auto pv_run = [&](const uint8_t* kb, const bf16x8 (&pb)[2], i16x8 (&v)[DV + 1], auto&& extra) {
       static_for<32>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
-        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(cb + DV);
+        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(kb, cb + DV);
         const bf16x8 va = __builtin_bit_cast(bf16x8, v[cb % (DV + 1)]);
         OBlock<2 * cb + 0>::mfma(va, pb[0]);
         __builtin_amdgcn_sched_barrier(0);
@@ -654,7 +665,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     bf16x8 pb[2];
     {
       f32x4 s0[4];
-      qk_tile(smem, s0, [](int) {});
+      qk_tile(smem, s0, [](int) {}, [] {}, true);
       const bool nm0 = kv0 + kTile > lim_wave;
 #pragma unroll
       for (int step = 0; step < kSoftmaxSteps; ++step) softmax_step(step, s0, nm0, kv0);
@@ -680,26 +691,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- QK^T of tile it+1, copies of tile it+3 between its MFMAs ----
-      auto copy_step = [&](int k) {
-        if ((k & 7) == 4 && (k >> 3) < kLoadsPerWave) {
-          static_for<kLoadsPerWave>([&](auto ic) {
-            if (decltype(ic)::value == (k >> 3)) dma(ic, nsrc, nbuf);
-          });
-        }
+      // Copies 0..4 of tile it+3 go between QK^T MFMAs, copies 5..8 between
+      // the first PV MFMAs (before the softmax steps start).
+      auto copy_at = [&](int i) {
+        static_for<kLoadsPerWave>([&](auto ic) {
+          if (decltype(ic)::value == i) dma(ic, nsrc, nbuf);
+        });
       };
+      i16x8 v[DV + 1];
       f32x4 s_next[4];
       if (has_next) {
-        qk_tile(kb_next, s_next, copy_step);
+        qk_tile(
+            kb_next, s_next, [&](int k) { if ((k & 15) == 4) copy_at(k >> 4); }, [&] { pv_prefetch(kb, v); }, false);
       } else {
         dma_all(nsrc, nbuf);
+        pv_prefetch(kb, v);
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- PV of tile it, softmax of tile it+1 between its MFMAs ----
+      // ---- PV of tile it, softmax of tile it+1 between its MFMAs (from
+      //      column block 4 on: by then the QK^T results are readable) ----
       if (has_next) {
         const bool nm = tb + 2 * kTile > lim_wave;
-        pv_tile(kb, pb, [&](int cb) {
-          if (cb < kSoftmaxSteps) softmax_step(cb, s_next, nm, tb + kTile);
+        pv_run(kb, pb, v, [&](int cb) {
+          if (cb < kLoadsPerWave - 5) {
+            copy_at(5 + cb);
+          } else {
+            softmax_step(cb - (kLoadsPerWave - 5), s_next, nm, tb + kTile);
+          }
         });
         // A row whose reference moved rescales everything accumulated so far
         // (tiles <= it).
@@ -710,7 +729,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
         any_scale = false;
         pack_p(pb);
       } else {
-        pv_tile(kb, pb, [](int) {});
+        pv_run(kb, pb, v, [](int) {});
       }
       // Pages of the tile the next iteration copies.  Looked up here, after
       // the last LDS read of the iteration: a scalar load in flight would make

@@ -6,6 +6,8 @@ wait counts.  These checks read the compiled assembly and verify what the
 kernel's comments promise:
   * no VALU instruction writes an MFMA operand (or result register) less than
     two wait states before the MFMA;
+  * no VALU instruction reads or writes a VGPR an MFMA writes less than 19
+    wait states after the MFMA (the longest MFMA-result latency);
   * the registers of the asynchronous query loads are not touched between the
     load and the first explicit vmcnt wait after it;
   * every vmcnt wait in the decode kernel is one the source writes explicitly
@@ -84,6 +86,30 @@ def mfma_hazards(body: list) -> list:
                     break
             need -= 1
             j -= 1
+    return bad
+
+
+def mfma_result_hazards(body: list, need: int = 19) -> list:
+    """(mfma, valu) pairs where VALU touches an MFMA's VGPR result too early."""
+    bad = []
+    for i, t in enumerate(body):
+        op, ops = _split(t)
+        if not op.startswith("v_mfma") or not ops or not ops[0].startswith("v"):
+            continue
+        dst = _regs(ops[0])
+        left, j = need, i + 1
+        while left > 0 and j < len(body):
+            uop, uops = _split(body[j])
+            if uop == "s_nop":
+                left -= int(uops[0], 0) + 1
+                j += 1
+                continue
+            if uop.startswith("v_") and not uop.startswith("v_mfma"):
+                if any(_regs(o) & dst for o in uops):
+                    bad.append((t, body[j]))
+                    break
+            left -= 1
+            j += 1
     return bad
 
 

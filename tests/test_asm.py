@@ -41,6 +41,11 @@ def test_no_valu_to_mfma_hazards(asm):
         assert asm_checks.mfma_hazards(body) == []
 
 
+def test_no_mfma_result_to_valu_hazards(asm):
+    for body in asm_checks.kernel_bodies(asm):
+        assert asm_checks.mfma_result_hazards(body) == []
+
+
 def test_async_query_loads_untouched_until_waited(asm):
     for body in asm_checks.kernel_bodies(asm):
         assert sum(t.startswith("global_load_dwordx4") for t in body) == 32
