@@ -877,6 +877,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
   }
 }
 
+// Combine for requests split into at most kCombineSmallMax pieces: one wave
+// per row (4 rows per workgroup).  Lane l owns stored positions 8l .. 8l+7 (as
+// in combine_kernel); every partial value of the row and the per-partial lse
+// and scale (lane s holds partial s) are loaded at once, so the row costs one
+// memory round trip.  Weights exp(lse_s - lse) f_s are broadcast from lane s.
+constexpr int kCombineSmallMax = 16;
+__global__ __launch_bounds__(256) void combine_small_kernel(const CombineJob* __restrict__ jobs,
+                                                             const uint16_t* __restrict__ ws_o,
+                                                             const float* __restrict__ ws_lse,
+                                                             const float* __restrict__ ws_f, int32_t rows,
+                                                             int32_t rpb, int32_t nrb, float* __restrict__ out,
+                                                             float* __restrict__ lse) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const CombineJob job = jobs[blockIdx.x];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int rb = row / rpb, rl = row - rb * rpb;
+  auto ri_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
+  const int n = job.n;  // <= kCombineSmallMax (checked on the host)
+
+  f16x8 v[kCombineSmallMax];
+#pragma unroll
+  for (int s = 0; s < kCombineSmallMax; ++s)
+    if (s < n) v[s] = *reinterpret_cast<const f16x8*>(ws_o + ri_of(s) * 512 + 8 * lane);
+  const float lse_s = lane < n ? ws_lse[ri_of(lane)] : -INFINITY;
+  const float f_s = lane < n ? ws_f[ri_of(lane)] : 0.f;
+
+  float m = lse_s;
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const bool any_nan = __any(lse_s != lse_s);  // fmaxf drops NaN; a NaN partial must stay loud
+  float z = (m != -INFINITY && lane < n) ? __expf(lse_s - m) : 0.f;
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+  const float lse_v = any_nan ? NAN : (m == -INFINITY ? -INFINITY : m + __logf(z));
+  const bool live = !any_nan && m != -INFINITY;
+  const float w_s = (live && lane < n) ? __expf(lse_s - lse_v) * f_s : 0.f;
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kCombineSmallMax; ++s) {
+    if (s < n) {
+      const float w = __shfl(w_s, s);
+      acc0 += w * f32x4{(float)v[s][0], (float)v[s][1], (float)v[s][2], (float)v[s][3]};
+      acc1 += w * f32x4{(float)v[s][4], (float)v[s][5], (float)v[s][6], (float)v[s][7]};
+    }
+  }
+  if (any_nan) {
+    acc0 = f32x4{NAN, NAN, NAN, NAN};
+    acc1 = acc0;
+  }
+  float* dst = out + ((int64_t)job.b * rows + row) * 512 + 32 * (lane >> 2) + 4 * (lane & 3);
+  *reinterpret_cast<f32x4*>(dst) = acc0;
+  *reinterpret_cast<f32x4*>(dst + 16) = acc1;
+  if (lane == 0) lse[(int64_t)job.b * rows + row] = lse_v;
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -1153,10 +1209,15 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void
   const mla::PlanData& d = plan->d;
   if (!d.jobs.empty()) {
     const char* base = static_cast<const char*>(plan->dev);
-    hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)d.rows), dim3(256), 0,
-                       static_cast<hipStream_t>(stream),
-                       reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs), ws.o, ws.lse, ws.f, d.rows,
-                       d.v.rows_per_block(), d.nrb, out, lse);
+    const mla::CombineJob* jobs = reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs);
+    if (d.max_pieces <= mla::kCombineSmallMax)
+      hipLaunchKernelGGL(mla::combine_small_kernel, dim3((unsigned)d.jobs.size(), (unsigned)((d.rows + 3) / 4)),
+                         dim3(256), 0, static_cast<hipStream_t>(stream), jobs, ws.o, ws.lse, ws.f, d.rows,
+                         d.v.rows_per_block(), d.nrb, out, lse);
+    else
+      hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)d.rows), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), jobs, ws.o, ws.lse, ws.f, d.rows, d.v.rows_per_block(),
+                         d.nrb, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }

@@ -213,7 +213,10 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
   }
 
   for (int32_t b = 0; b < batch; ++b)
-    if (pieces_of[b] > 1) p.jobs.push_back(CombineJob{b, first_partial[b], pieces_of[b], 0});
+    if (pieces_of[b] > 1) {
+      p.jobs.push_back(CombineJob{b, first_partial[b], pieces_of[b], 0});
+      p.max_pieces = std::max(p.max_pieces, pieces_of[b]);
+    }
   return kOk;
 }
 

@@ -46,6 +46,7 @@ struct PlanData {
   Variant v{};
   int32_t max_pages = 0;  // max_b ceil(L_b / page)
   int32_t num_partials = 0;
+  int32_t max_pieces = 0;   // most pieces of one split request (combine kernel choice)
   int32_t grid = 0;       // decode-kernel workgroups (>= wgs actually used)
   std::vector<int32_t> lens;
   std::vector<Segment> segs;

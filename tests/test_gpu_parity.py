@@ -11,6 +11,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import decode_attention_absorbed_amd as mla  # noqa: E402
+from decode_attention_absorbed_amd import binding as bnd  # noqa: E402
 from oracle import mla_decode_ref  # noqa: E402
 from workloads import CONFIGS, make_config, make_inputs, poison_tails, poison_unreferenced  # noqa: E402
 
@@ -90,6 +91,18 @@ def test_forced_split_counts_agree(dev, num_cus):
     assert np.max(np.abs(out - base_o)) < OUT_MAX_ABS
     assert np.linalg.norm(out - base_o) / np.linalg.norm(base_o) < OUT_REL_L2
     assert np.max(np.abs(lse - base_l)) < 1e-5
+
+
+@pytest.mark.parametrize("L,num_cus", [(1024, 8), (8192, 256)], ids=["few-pieces", "many-pieces"])
+def test_both_combine_kernels(dev, L, num_cus):
+    # at most 16 pieces per request take the one-wave-per-row combine, more the
+    # four-waves-per-row one; both must merge to the oracle
+    x = make_inputs(2, 128, 1, 64, [L, L // 2], seed=17)
+    plan = mla.mla_decode_plan(x.seq_lens, x.q_len, x.heads, x.page, num_cus)
+    pieces = plan.query(bnd.MLA_Q_NUM_PARTIALS)
+    assert (pieces <= 2 * 16) if L == 1024 else (pieces > 2 * 16)
+    out, lse = run_gpu(x, dev, plan=plan)
+    compare(out, lse, *oracle(x), what=f"L={L} num_cus={num_cus} pieces={pieces}")
 
 
 # ---- the five named workloads at full size, oracle on sampled requests ------------------
