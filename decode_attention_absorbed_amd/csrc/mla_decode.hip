@@ -168,6 +168,14 @@ __device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, uint
                : "memory");
 }
 
+// 4-byte global load into a VGPR, invisible to the compiler's wait counts
+// (waited for explicitly).
+__device__ __forceinline__ int load4(const int32_t* src) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+  return v;
+}
+
 // 16-byte global load into VGPRs, invisible to the compiler's wait counts
 // (the explicit wait before the first QK^T covers it).
 __device__ __forceinline__ bf16x8 load16(const void* src) {
@@ -372,9 +380,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
   for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
     const Segment sg = segs[si];
     const int b = sg.b, kv0 = sg.kv_begin, kv1 = sg.kv_end;
+    const int32_t* bt_row = block_table + (int64_t)b * bt_stride;
+
+    // The piece's first 64 block-table entries sit in one register, lane i
+    // holding page first_pg + i (lanes past the piece repeat its last page),
+    // loaded once per piece; the tile loop reads them with readlane, so no
+    // memory load (and no wait on one) sits between the LDS reads of the
+    // loop.  Pages beyond the first 64 of a piece come from scalar loads.
+    // The load is issued before the query loads; it is waited for (vmcnt in
+    // order) once only the query loads are still in flight.
+    const int first_pg = kv0 >> page_log2;
+    const int last_pg = (kv1 - 1) >> page_log2;
+    int pg_lane = load4(bt_row + min(first_pg + lane, last_pg));
+
+    // Query rows as the B operand: q[16hb + ks] holds dims 32ks + 8grp .. +7
+    // of row hb (c_kv part, registers); the rope part is copied to this
+    // wave's LDS slice (4 copies of 1 KB: slot p = row p/8, chunk p%8).  Rows
+    // past the end load row 0: their scores are masked and they are never
+    // stored.  Only this wave reads its slice, so the copies need no barrier.
+    bf16x8 q[2 * kNopeSteps];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int qrow = row_ok[hb] ? row[hb] : 0;
+      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < kNopeSteps; ++ks) q[kNopeSteps * hb + ks] = load16(qn + 32 * ks);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int pidx = n * 64 + lane;
+      const int r = pidx >> 3;
+      const int c = (pidx & 7) ^ ((r >> 1) & 7);
+      const int qr = wave_row0 + r;
+      const int qrow = qr < rows ? qr : 0;
+      dma16(q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * c, lds_addr(qpe_lds + wave * kQpeWaveBytes + n * 1024));
+    }
+
     const int L = seq_lens[b];
     const bool bad_len = (L != planned_lens[b]);
-    const int32_t* bt_row = block_table + (int64_t)b * bt_stride;
 
     // Keys each of this lane's rows may see inside the piece: [kv0, lim).
     int lim[2];
@@ -383,15 +426,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // A tile starting at key tb needs masking iff tb + kTile > lim_wave.
     const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
 
-    // Block-table entries of a tile (scalar loads, checked when used).
-    // The piece's first 64 block-table entries sit in one register, lane i
-    // holding page first_pg + i, loaded once per piece; the tile loop reads
-    // them with readlane, so no memory load (and no wait on one) sits between
-    // the LDS reads of the loop.  Pages beyond the first 64 of a piece come
-    // from scalar loads.
-    const int first_pg = kv0 >> page_log2;
-    const int npg_piece = ((kv1 - 1) >> page_log2) - first_pg + 1;
-    const int pg_lane = lane < npg_piece ? bt_row[first_pg + lane] : 0;
+    // Block-table entries of a tile (checked when used).
     auto page_at = [&](int pidx) {
       const int rel = pidx - first_pg;
       return rel < 64 ? __builtin_amdgcn_readlane(pg_lane, rel) : bt_row[pidx];
@@ -452,33 +487,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // tiles of this one land in LDS.
     __syncthreads();
 
-    const int last_tile = ntiles - 1;
-    // Tile 0 first, then the queries, then tiles 1 and 2: the first wait
-    // (two tiles still in flight) covers tile 0 and the queries.
-    dma_all(tile_src(kv0, checked(fetch_pages(kv0))), smem);
+    // Page ids have landed once only the 36 query copies are in flight.
+    wait_vmem<2 * kNopeSteps + 4>();
+    asm volatile("" : "+v"(pg_lane));
 
-    // Query rows as the B operand: q[16hb + ks] holds dims 32ks + 8grp .. +7
-    // of row hb (c_kv part, registers); the rope part is copied to this
-    // wave's LDS slice (4 copies of 1 KB: slot p = row p/8, chunk p%8).  Rows
-    // past the end load row 0: their scores are masked and they are never
-    // stored.
-    bf16x8 q[2 * kNopeSteps];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int qrow = row_ok[hb] ? row[hb] : 0;
-      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < kNopeSteps; ++ks) q[kNopeSteps * hb + ks] = load16(qn + 32 * ks);
-    }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int pidx = n * 64 + lane;
-      const int r = pidx >> 3;
-      const int c = (pidx & 7) ^ ((r >> 1) & 7);
-      const int qr = wave_row0 + r;
-      const int qrow = qr < rows ? qr : 0;
-      dma16(q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * c, lds_addr(qpe_lds + wave * kQpeWaveBytes + n * 1024));
-    }
+    const int last_tile = ntiles - 1;
+    dma_all(tile_src(kv0, checked(fetch_pages(kv0))), smem);
 
     // Software pipeline over tiles (4 LDS stages).  Iteration `it`:
     //   QK^T of tile it+1, with the copies of tile it+3 issued between its
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
                                          5, 6, 7);
     };
 
-    // Tile 0 and the query rows (issued before tiles 1 and 2) have landed
+    // The query rows and tile 0 (issued before tiles 1 and 2) have landed
     // once two tiles of copies are still in flight.  The empty asm statements tie the
     // query registers to this point: the loads fill them asynchronously, so
     // nothing may read, copy or reuse them before the wait.

@@ -8,8 +8,8 @@ kernel's comments promise:
     two wait states before the MFMA;
   * no VALU instruction reads or writes a VGPR an MFMA writes less than 19
     wait states after the MFMA (the longest MFMA-result latency);
-  * the registers of the asynchronous query loads are not touched between the
-    load and the first explicit vmcnt wait after it;
+  * the registers of the asynchronous query and page-id loads are not touched
+    between the load and the first explicit vmcnt wait after it;
   * every vmcnt wait in the decode kernel is one the source writes explicitly
     (the compiler adds none: an extra one would serialize the copy pipeline).
 """
@@ -118,7 +118,7 @@ def async_load_violations(body: list) -> list:
     bad = []
     for i, t in enumerate(body):
         op, ops = _split(t)
-        if op != "global_load_dwordx4" or len(ops) < 2 or ops[-1] != "off":
+        if op not in ("global_load_dwordx4", "global_load_dword") or len(ops) < 2 or ops[-1] != "off":
             continue
         dst = _regs(ops[0])
         for u in body[i + 1 :]:

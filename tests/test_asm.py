@@ -53,8 +53,9 @@ def test_async_query_loads_untouched_until_waited(asm):
 
 
 def test_only_explicit_vmcnt_waits(asm):
-    # 18 = two tiles of copies in flight (prologue), 9 = one tile (loop), 0 = drain
+    # 36 = query copies in flight (page ids landed), 18 = two tiles of copies
+    # in flight (prologue), 9 = one tile (loop), 0 = drain
     for body in asm_checks.kernel_bodies(asm):
         waits = asm_checks.vmcnt_waits(body)
         counts = sorted({int(w.split("vmcnt(")[1].split(")")[0]) for w in waits})
-        assert counts == [0, 9, 18], waits
+        assert counts == [0, 9, 18, 36], waits
