@@ -591,18 +591,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     float mx[2], mu[2] = {kMuFloor, kMuFloor};
     bf16x2 pw[2][4];  // P^T operand under construction: K slots 2m, 2m+1
     float p_even = 0.f;
+    float xt[2];  // exponent of the element whose exp comes next
 
     // Softmax of one tile of raw scores s (s[2kb + hb][i] = key tb_s + 16kb +
     // 4grp + i, row block hb), as kSoftmaxSteps short steps so that it can be
     // spread between MFMAs:
     //   0-3: mask block (kb, hb)'s keys past the row's limit (only on tiles
-    //        that need it), 4-5: row block max, 6-9: max over the 4 lane
-    //        groups,
-    //   10-11: reference update (a row moves its reference only when its
+    //        that need it), 4: both row blocks' max, 5-8: max over the 4
+    //        lane groups,
+    //   9-10: reference update (a row moves its reference only when its
     //      maximum grows by more than kRescaleThreshold; the first finite
     //      maximum needs no rescale because nothing has been accumulated yet),
-    //   12-27: p = 2^(s * scale - mu), running sum, bf16 pairs of P^T (K slot
-    //      j of row block hb is s[2(j/4) + hb][j%4]).
+    //   11-27: p = 2^(s * scale - mu), running sum, bf16 pairs of P^T (K slot
+    //      j of row block hb is s[2(j/4) + hb][j%4]); software-pipelined so
+    //      that a step's exp never waits on the same step's fma.
     auto softmax_step = [&](int step, f32x4(&s)[4], bool need_mask, int tb_s) {
       if (step < 4) {
         const int kbk = step >> 1, hb = step & 1;
@@ -613,21 +615,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
             s[2 * kbk + hb][i] = tok < lim[hb] ? s[2 * kbk + hb][i] : -INFINITY;
           }
         }
-      } else if (step < 6) {
-        const int hb = step - 4;
-        const f32x4& x0 = s[hb];
-        const f32x4& x1 = s[2 + hb];
-        mx[hb] = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], x1[3]));
-      } else if (step < 10) {
-        const int hb = (step - 6) >> 1;
-        mx[hb] = (step & 1) ? group_max16(mx[hb]) : group_max32(mx[hb]);
-      } else if (step < 12) {
+      } else if (step == 4) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const f32x4& x0 = s[hb];
+          const f32x4& x1 = s[2 + hb];
+          mx[hb] = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], x1[3]));
+        }
+      } else if (step < 9) {
+        const int hb = (step - 5) >> 1;
+        mx[hb] = (step & 1) ? group_max32(mx[hb]) : group_max16(mx[hb]);
+      } else if (step < 11) {
         {
           // mu = max(m_ref, kMuFloor) is the reference actually subtracted,
           // so alpha = 2^(mu_old - mu_new) needs no case for -inf: it is 1
           // without an update and 0 for a row's first finite maximum (when
           // nothing has been accumulated for that row).
-          const int hb = step - 10;
+          const int hb = step - 9;
           const float m = mx[hb] * scale_log2;
           const bool upd = m > m_ref[hb] + kRescaleThreshold;
           const float m_new = upd ? m : m_ref[hb];
@@ -639,24 +643,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           mu[hb] = mu_new;
         }
       } else if (step < kSoftmaxSteps) {
-        const int j = step - 12;
-        const int hb = j >> 3, jj = j & 7;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * (jj >> 2) + hb][jj & 3], scale_log2, -mu[hb]));
-        l_part[hb] += p;
-        if (jj & 1) {
-          pw[hb][jj >> 1] = bf16x2{(__bf16)p_even, (__bf16)p};
-          asm volatile("" : "+v"(pw[hb][jj >> 1]));  // pack now, not at the end
-        } else {
-          p_even = p;
+        const int j = step - 11;  // 0..16: exp of element j-1, fma of element j
+        if (j >= 1) {
+          const int k = j - 1, hb = k >> 3, kk = k & 7;
+          const float p = __builtin_amdgcn_exp2f(xt[k & 1]);
+          l_part[hb] += p;
+          if (kk & 1) {
+            pw[hb][kk >> 1] = bf16x2{(__bf16)p_even, (__bf16)p};
+            asm volatile("" : "+v"(pw[hb][kk >> 1]));  // pack now, not at the end
+          } else {
+            p_even = p;
+          }
+        }
+        if (j < 16) {
+          const int hb = j >> 3, jj = j & 7;
+          xt[j & 1] = __builtin_fmaf(s[2 * (jj >> 2) + hb][jj & 3], scale_log2, -mu[hb]);
         }
       }
     };
+    auto pack_half = [&](bf16x8 (&pb)[2], int hb) {
+      pb[hb] = __builtin_shufflevector(__builtin_shufflevector(pw[hb][0], pw[hb][1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pw[hb][2], pw[hb][3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
+                                       6, 7);
+    };
     auto pack_p = [&](bf16x8 (&pb)[2]) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        pb[hb] = __builtin_shufflevector(__builtin_shufflevector(pw[hb][0], pw[hb][1], 0, 1, 2, 3),
-                                         __builtin_shufflevector(pw[hb][2], pw[hb][3], 0, 1, 2, 3), 0, 1, 2, 3, 4,
-                                         5, 6, 7);
+      pack_half(pb, 0);
+      pack_half(pb, 1);
     };
 
     // The query rows and tile 0 (issued before tiles 1 and 2) have landed
@@ -715,9 +727,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       i16x8 v[DV + 1];
       f32x4 s_next[4];
       if (has_next) {
+        // P of tile it (from the previous iteration's softmax) becomes the PV
+        // operand between QK^T MFMAs, where the VALU is otherwise idle.
         qk_tile(
-            kb_next, s_next, [&](int k) { if ((k & 15) == 4) copy_at(k >> 4); }, [&] { pv_prefetch(kb, v); }, false);
+            kb_next, s_next,
+            [&](int k) {
+              if ((k & 15) == 4) copy_at(k >> 4);
+              if (k == 10 || k == 26) pack_half(pb, k == 26);
+            },
+            [&] { pv_prefetch(kb, v); }, false);
       } else {
+        pack_p(pb);
         dma_all(nsrc, nbuf);
         pv_prefetch(kb, v);
       }
@@ -741,7 +761,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           o_scale_all(alpha[0], alpha[1]);
         }
         any_scale = false;
-        pack_p(pb);
       } else {
         pv_run(kb, pb, v, [](int) {});
       }
