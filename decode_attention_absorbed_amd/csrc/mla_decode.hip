@@ -15,10 +15,10 @@
 //    (global_load_lds_dwordx4) into a ring of 4 buffers; while tile i is
 //    computed, tiles i+1 .. i+3 are resident or in flight (about 110 KB per
 //    CU, enough to cover HBM latency at full bandwidth).  One barrier per tile;
-//  * a cached row is 72 chunks of 16 bytes; inside each aligned group of 8
-//    chunks, chunk c of key row t is stored at c ^ swz(t).  The swizzle makes
-//    both the row reads of QK^T (16 rows, same chunk) and the transposed reads
-//    of PV (8 rows x 2 chunks per half wave) hit distinct banks;
+//  * a cached row is 72 chunks of 16 bytes; LDS holds the tile column major
+//    (all 32 rows of a chunk together) with the two row halves of odd chunks
+//    swapped, so that both the row reads of QK^T and the transposed reads of
+//    PV hit distinct banks (layout below);
 //  * all products are v_mfma_f32_16x16x32_bf16.  (The 32x32x16 form needs a
 //    36-step dependent chain per tile for QK^T, which runs at a third of the
 //    matrix rate; the 16x16 form gives four independent 18-step chains, and a
@@ -91,14 +91,18 @@ static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of
 static_assert(kLoadsPerWave - 5 + kSoftmaxSteps == 32, "PV gaps: 4 copies, then the softmax steps");
 
 // LDS layout of a 32-key tile (36 KB), column major: the 16-byte chunk c
-// (0..71) of key row t (0..31) sits at slot 32c + (t ^ 8(c & 1)).
+// (0..71) of key row t (0..31) sits at slot 32c + (t ^ 16(c & 1)).
+// gfx950's LDS has 128 four-byte banks (512 bytes) and serves a 128-bit read
+// 32 lanes at a time, so a read is conflict-free when each half wave covers
+// 512 distinct bytes modulo 512.
 //  * a 1 KB copy n fills slots 64n .. 64n+63: lane l brings chunk 2n + l/32 of
-//    key row (l % 32) ^ 8(l / 32), so a lane's source row is the same for every
+//    key row (l % 32) ^ 16(l / 32), so a lane's source row is the same for every
 //    copy and the copies of a tile differ only by a constant offset;
 //  * QK^T reads 16 consecutive key rows of one chunk per 16 lanes (256
-//    contiguous bytes);
-//  * PV's transposed reads take 8 rows x 2 chunks per half wave; the row xor
-//    on odd chunks puts the two chunks on different banks.
+//    contiguous bytes); a half wave reads chunks 2j and 2j + 1, which the
+//    half swap puts 256 bytes apart modulo 512;
+//  * PV's transposed reads take 8 rows x 2 chunks per half wave (8 bytes per
+//    lane, 256 bytes per half wave), again in distinct banks.
 
 // Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 // permlaneX_swap(x, x) returns the pair {x[l & ~X], x[l | X]} in some order,
@@ -355,27 +359,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
   // Per-lane LDS byte offsets (within a stage) of the operand reads; the
   // remaining terms are compile-time offsets.
   // QK^T, A operand = key rows: key 16kb + l16, chunk 4ks + grp:
-  //   qk_base + 2048 ks + 256 kb.
-  const int qk_off = 512 * grp + 16 * (l16 ^ (8 * (grp & 1)));
+  //   qk_off0 + 2048 ks for key block 0; key block 1 sits in the other half
+  //   of the chunk (odd chunks hold rows 16.. first): bit 8 flipped.
+  const int qk_off0 = 512 * grp + 16 * l16 + 256 * (grp & 1);
   // PV, A operand = V^T via transposed reads.  Within 16-lane group grp, lane
   // l16 addresses key row 16rd + 4grp + l16/4, columns 16cb + 4(l16%4) .. +3
   // (chunk 2cb + (l16%4)/2, byte 8(l16%2)); the read hands it column 16cb + l16
   // of those 4 keys (K slots 4rd .. 4rd+3 of the group):
-  //   pv_base + 1024 cb + 256 rd.
+  //   pv_off0 + 1024 cb for rd = 0, in row half hsel of the chunk; rd = 1
+  //   reads the other half (bit 8 flipped).
   const int hsel = (l16 >> 1) & 1;
-  const int pv_off = 512 * hsel + 16 * ((4 * grp + (l16 >> 2)) ^ (8 * hsel)) + 8 * (l16 & 1);
+  const int pv_off0 = 768 * hsel + 16 * (4 * grp + (l16 >> 2)) + 8 * (l16 & 1);
   // Tile copies: wave w issues copies n = 4i + w (i = 0..8) of a tile; lane l
   // reads key row dma_row, bytes dma_col + 128 i of it.
-  const int dma_row = (lane & 31) ^ (8 * (lane >> 5));
+  const int dma_row = (lane & 31) ^ (16 * (lane >> 5));
   const int dma_col = 16 * (lane >> 5) + 32 * wave;
   // Rope part of the query (dims 512..575) in LDS: row r (0..31) of wave w
   // at w * 4096 + 128 r, its 16-byte chunk c at slot c ^ ((r >> 1) & 7), so
-  // that 16 rows reading one chunk hit distinct banks.  B operand of step
-  // 16 + e, row block hb: row 16hb + l16, chunk 4e + grp.
-  int qpe_base[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    qpe_base[e] = (int)lds_addr(qpe_lds) + wave * kQpeWaveBytes + l16 * 128 + 16 * ((4 * e + grp) ^ ((l16 >> 1) & 7));
+  // that a half wave (16 rows, chunks 4e and 4e + 1) hits distinct banks.
+  // B operand of step 16 + e, row block hb: row 16hb + l16, chunk 4e + grp;
+  // e = 1 is e = 0 with address bit 6 flipped.
+  const uint32_t qpe_base = lds_addr(qpe_lds) + wave * kQpeWaveBytes + l16 * 128 + 16 * (grp ^ ((l16 >> 1) & 7));
 
   for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
     const Segment sg = segs[si];
@@ -523,13 +527,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       constexpr int D = kQkDepth;
       bf16x8 a[D + 1][2];
       bf16x8 qb[2][2];  // rope steps: [e][hb]
+      // Stage bases are multiples of 512 bytes: bit 8 of the sum is the lane's.
+      const uint32_t k0 = lds_addr(kb) + qk_off0, k1 = k0 ^ 256u;
       auto read_step = [&](int ks) {
-        a[ks % (D + 1)][0] = *reinterpret_cast<const bf16x8*>(kb + qk_off + 2048 * ks);
-        a[ks % (D + 1)][1] = *reinterpret_cast<const bf16x8*>(kb + qk_off + 2048 * ks + 256);
+        a[ks % (D + 1)][0] = *LDS_AS(const bf16x8, (uintptr_t)(k0 + 2048 * ks));
+        a[ks % (D + 1)][1] = *LDS_AS(const bf16x8, (uintptr_t)(k1 + 2048 * ks));
         if (ks >= kNopeSteps) {
           const int e = ks - kNopeSteps;
-          qb[e][0] = *LDS_AS(const bf16x8, (uintptr_t)qpe_base[e]);
-          qb[e][1] = *LDS_AS(const bf16x8, (uintptr_t)(qpe_base[e] + 2048));
+          const uint32_t qa = e ? qpe_base ^ 64u : qpe_base;
+          qb[e][0] = *LDS_AS(const bf16x8, (uintptr_t)qa);
+          qb[e][1] = *LDS_AS(const bf16x8, (uintptr_t)(qa + 2048));
         }
       };
 #pragma unroll
@@ -558,20 +565,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // run inside the previous phase); pv_run does the 32 column blocks and
     // calls `extra(cb)` between the two MFMAs of each.
     constexpr int DV = kPvDepth;
-    auto read_v = [&](const uint8_t* kb, int cb) {
-      const uint8_t* p0 = kb + pv_off + 1024 * cb;
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, p0 + 256));
+    struct PvBase {
+      uint32_t r0, r1;  // LDS addresses of the rd = 0 and rd = 1 reads of column block 0
+    };
+    auto pv_base = [&](const uint8_t* kb) {
+      const uint32_t r0 = lds_addr(kb) + pv_off0;
+      return PvBase{r0, r0 ^ 256u};
+    };
+    auto read_v = [&](const PvBase& vb, int cb) {
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)(vb.r0 + 1024 * cb)));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)(vb.r1 + 1024 * cb)));
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto pv_prefetch = [&](const uint8_t* kb, i16x8 (&v)[DV + 1]) {
+    auto pv_prefetch = [&](const PvBase& vb, i16x8 (&v)[DV + 1]) {
 #pragma unroll
-      for (int d = 0; d < DV; ++d) v[d] = read_v(kb, d);
+      for (int d = 0; d < DV; ++d) v[d] = read_v(vb, d);
     };
-    auto pv_run = [&](const uint8_t* kb, const bf16x8 (&pb)[2], i16x8 (&v)[DV + 1], auto&& extra) {
+    auto pv_run = [&](const PvBase& vb, const bf16x8 (&pb)[2], i16x8 (&v)[DV + 1], auto&& extra) {
       static_for<32>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
-        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(kb, cb + DV);
+        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(vb, cb + DV);
         const bf16x8 va = __builtin_bit_cast(bf16x8, v[cb % (DV + 1)]);
         OBlock<2 * cb + 0>::mfma(va, pb[0]);
         __builtin_amdgcn_sched_barrier(0);
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       __syncthreads();
 
       const int tb = kv0 + it * kTile;
-      const uint8_t* kb = smem + (it % kStages) * kStageBytes;             // tile it (PV)
+      const PvBase vb = pv_base(smem + (it % kStages) * kStageBytes);     // tile it (PV)
       const uint8_t* kb_next = smem + ((it + 1) % kStages) * kStageBytes;  // tile it+1 (QK^T)
       const int nt = it + 3;                                               // tile to copy now
       const int tb_c = kv0 + min(nt, last_tile) * kTile;
@@ -735,11 +748,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
               if ((k & 15) == 4) copy_at(k >> 4);
               if (k == 10 || k == 26) pack_half(pb, k == 26);
             },
-            [&] { pv_prefetch(kb, v); }, false);
+            [&] { pv_prefetch(vb, v); }, false);
       } else {
         pack_p(pb);
         dma_all(nsrc, nbuf);
-        pv_prefetch(kb, v);
+        pv_prefetch(vb, v);
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -747,7 +760,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       //      column block 4 on: by then the QK^T results are readable) ----
       if (has_next) {
         const bool nm = tb + 2 * kTile > lim_wave;
-        pv_run(kb, pb, v, [&](int cb) {
+        pv_run(vb, pb, v, [&](int cb) {
           if (cb < kLoadsPerWave - 5) {
             copy_at(5 + cb);
           } else {
@@ -762,7 +775,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
         }
         any_scale = false;
       } else {
-        pv_run(kb, pb, v, [](int) {});
+        pv_run(vb, pb, v, [](int) {});
       }
       // Pages of the tile the next iteration copies.  Looked up here, after
       // the last LDS read of the iteration: a scalar load in flight would make
@@ -790,12 +803,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
         float inv = l_tot[hb] > 0.f ? 1.f / l_tot[hb] : 0.f;
         if (bad_len) inv = NAN;
         if (!row_ok[hb]) continue;
-        float* dst = out + ((int64_t)b * rows + row[hb]) * 512 + 4 * grp;
+        // Computed here, not hoisted above the tile loop (it would hold two
+        // registers through the loop).
+        int r = row[hb];
+        asm volatile("" : "+v"(r));
+        const int64_t oi = (int64_t)b * rows + r;
+        float* dst = out + oi * 512 + 4 * grp;
         if (hb == 0)
           o_store_rec<0, 0>(dst, inv);
         else
           o_store_rec<1, 0>(dst, inv);
-        if (grp == 0) lse[(int64_t)b * rows + row[hb]] = lse_v[hb];
+        if (grp == 0) lse[oi] = lse_v[hb];
       }
     } else {
       // Piece of a split request: the partial o = O / l is stored as O * 2^(15-e)
