@@ -88,6 +88,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kMuFloor = -1e30f;         // subtracted reference of a row with no visible key yet
 static_assert(kLoadsPerTile % kWaves == 0, "every wave issues the same number of copies");
+static_assert(2 * kPvDepth <= 4, "the V^T prefetch reads fit the four slots of the last QK^T step");
 static_assert(kLoadsPerWave - 5 + kSoftmaxSteps == 32, "PV gaps: 4 copies, then the softmax steps");
 
 // LDS layout of a 32-key tile (36 KB), column major: the 16-byte chunk c
@@ -264,6 +265,21 @@ __device__ __forceinline__ void o_scale_all(float alpha0, float alpha1) { o_scal
 // Wait out the MFMA write -> AGPR read latency before reading results.
 __device__ __forceinline__ void o_drain() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
 
+// 16-byte store that writes through this XCD's L2 (system-scope coherence
+// bits): the kernel's results are read by the next kernel anyway, and lines
+// left dirty in L2 would all be written back at the end of the kernel, after
+// the last workgroup, instead of while the other workgroups still run.  A
+// store of more than 8 bytes reads its data registers after issue, so no VALU
+// instruction may overwrite them in the next wait state; the compiler does not
+// see this store, hence the s_nop (checked on the assembly).
+template <typename V>
+__device__ __forceinline__ void store_wt(void* p, const V& v) {
+  static_assert(sizeof(V) == 16, "one 16-byte store");
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(__builtin_bit_cast(u32x4, v))
+               : "memory");
+}
+
 // Store the 32 blocks of row block HB, scaled: block (cb, HB) goes to
 // dst[16cb .. 16cb+3] (dst already points at this lane's 4 columns).
 template <int HB, int CB>
@@ -271,7 +287,7 @@ __device__ __forceinline__ void o_store_rec(float* dst, float inv) {
   if constexpr (CB < 32) {
     constexpr int r = 4 * (2 * CB + HB);
     f32x4 w = {o_get<r + 0>() * inv, o_get<r + 1>() * inv, o_get<r + 2>() * inv, o_get<r + 3>() * inv};
-    *reinterpret_cast<f32x4*>(dst + 16 * CB) = w;
+    store_wt(dst + 16 * CB, w);
     o_store_rec<HB, CB + 1>(dst, inv);
   }
 }
@@ -302,7 +318,7 @@ __device__ __forceinline__ void o_store_half_rec(_Float16* dst, float c) {
     f16x8 w = {(_Float16)(o_get<r0 + 0>() * c), (_Float16)(o_get<r0 + 1>() * c), (_Float16)(o_get<r0 + 2>() * c),
                (_Float16)(o_get<r0 + 3>() * c), (_Float16)(o_get<r1 + 0>() * c), (_Float16)(o_get<r1 + 1>() * c),
                (_Float16)(o_get<r1 + 2>() * c), (_Float16)(o_get<r1 + 3>() * c)};
-    *reinterpret_cast<f16x8*>(dst + 16 * CB) = w;
+    store_wt(dst + 16 * CB, w);
     o_store_half_rec<HB, CB + 2>(dst, c);
   }
 }
@@ -518,39 +534,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 
     // QK^T of one tile: acc[2kb + hb] = S^T block (keys 16kb.., rows 16hb..).
     // `extra(k)` (k = 4ks + j) is called between the MFMAs so that
-    // independent work issues while the matrix pipe runs; `tail()` before
-    // the MFMAs of the last step (the next phase's first LDS reads).  With
+    // independent work issues while the matrix pipe runs; `tail(j)` before
+    // MFMA j of the last step (the next phase's first LDS reads).  With
     // `drain`, the results are readable by VALU on return; without, the
     // caller keeps >= 19 instructions between the last MFMA and any VALU
     // access of acc (checked on the assembly).
+    // One wave issues at most one LDS read per MFMA slot: a second read
+    // right behind the first waits for the LDS issue port and holds back the
+    // next MFMA, so the reads of a step are spread over its four slots.
     auto qk_tile = [&](const uint8_t* kb, f32x4(&acc)[4], auto&& extra, auto&& tail, bool drain) {
       constexpr int D = kQkDepth;
       bf16x8 a[D + 1][2];
       bf16x8 qb[2][2];  // rope steps: [e][hb]
       // Stage bases are multiples of 512 bytes: bit 8 of the sum is the lane's.
       const uint32_t k0 = lds_addr(kb) + qk_off0, k1 = k0 ^ 256u;
-      auto read_step = [&](int ks) {
-        a[ks % (D + 1)][0] = *LDS_AS(const bf16x8, (uintptr_t)(k0 + 2048 * ks));
-        a[ks % (D + 1)][1] = *LDS_AS(const bf16x8, (uintptr_t)(k1 + 2048 * ks));
-        if (ks >= kNopeSteps) {
-          const int e = ks - kNopeSteps;
+      // Read of step ks issued in slot j: key block 0 (j = 0), key block 1
+      // (j = 2), and on rope steps the query's rope chunks (j = 1, 3).
+      auto read = [&](int ks, int j) {
+        if (j == 0) {
+          a[ks % (D + 1)][0] = *LDS_AS(const bf16x8, (uintptr_t)(k0 + 2048 * ks));
+        } else if (j == 2) {
+          a[ks % (D + 1)][1] = *LDS_AS(const bf16x8, (uintptr_t)(k1 + 2048 * ks));
+        } else if (ks >= kNopeSteps) {
+          const int e = ks - kNopeSteps, hb = j >> 1;
           const uint32_t qa = e ? qpe_base ^ 64u : qpe_base;
-          qb[e][0] = *LDS_AS(const bf16x8, (uintptr_t)qa);
-          qb[e][1] = *LDS_AS(const bf16x8, (uintptr_t)(qa + 2048));
+          qb[e][hb] = *LDS_AS(const bf16x8, (uintptr_t)(qa + 2048 * hb));
         }
       };
 #pragma unroll
-      for (int d = 0; d < D; ++d) read_step(d);
+      for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) read(d, j);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ++ks) {
-        if (ks + D < kQSteps) read_step(ks + D);
-        if (ks == kQSteps - 1) {
-          tail();
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          if (ks + D < kQSteps) read(ks + D, j);
+          if (ks == kQSteps - 1) tail(j);
           extra(4 * ks + j);
           const bf16x8& bq = ks < kNopeSteps ? q[kNopeSteps * (j & 1) + ks] : qb[ks - kNopeSteps][j & 1];
           s_mfma(acc[j], a[ks % (D + 1)][j >> 1], bq, ks == 0);
@@ -560,10 +581,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       if (drain) s_mfma_drain(acc);
     };
 
-    // O^T += V^T P^T for one tile, V^T read transposed from its stage.
-    // pv_prefetch issues the reads of the first kPvDepth column blocks (it may
-    // run inside the previous phase); pv_run does the 32 column blocks and
-    // calls `extra(cb)` between the two MFMAs of each.
+    // O^T += V^T P^T for one tile, V^T read transposed from its stage (two
+    // reads per column block, rd = 0 and 1, one per MFMA slot).
+    // pv_prefetch(i) issues read i (column block i/2, rd i%2) of the first
+    // kPvDepth column blocks (it runs inside the previous phase); pv_run does
+    // the 32 column blocks and calls `extra(cb)` between the two MFMAs of each.
     constexpr int DV = kPvDepth;
     struct PvBase {
       uint32_t r0, r1;  // LDS addresses of the rd = 0 and rd = 1 reads of column block 0
@@ -572,22 +594,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       const uint32_t r0 = lds_addr(kb) + pv_off0;
       return PvBase{r0, r0 ^ 256u};
     };
-    auto read_v = [&](const PvBase& vb, int cb) {
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)(vb.r0 + 1024 * cb)));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)(vb.r1 + 1024 * cb)));
-      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    auto read_v = [&](const PvBase& vb, int cb, int rd) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)((rd ? vb.r1 : vb.r0) + 1024 * cb)));
     };
-    auto pv_prefetch = [&](const PvBase& vb, i16x8 (&v)[DV + 1]) {
-#pragma unroll
-      for (int d = 0; d < DV; ++d) v[d] = read_v(vb, d);
+    auto pv_prefetch = [&](const PvBase& vb, i16x4 (&v)[DV + 1][2], int i) {
+      v[i >> 1][i & 1] = read_v(vb, i >> 1, i & 1);
     };
-    auto pv_run = [&](const PvBase& vb, const bf16x8 (&pb)[2], i16x8 (&v)[DV + 1], auto&& extra) {
+    auto pv_run = [&](const PvBase& vb, const bf16x8 (&pb)[2], i16x4 (&v)[DV + 1][2], auto&& extra) {
       static_for<32>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
-        if constexpr (cb + DV < 32) v[(cb + DV) % (DV + 1)] = read_v(vb, cb + DV);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, v[cb % (DV + 1)]);
+        constexpr int nb = (cb + DV) % (DV + 1), b = cb % (DV + 1);
+        if constexpr (cb + DV < 32) v[nb][0] = read_v(vb, cb + DV, 0);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[b][0], v[b][1], 0, 1, 2, 3, 4, 5, 6, 7));
         OBlock<2 * cb + 0>::mfma(va, pb[0]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (cb + DV < 32) v[nb][1] = read_v(vb, cb + DV, 1);
         extra(cb);
         OBlock<2 * cb + 1>::mfma(va, pb[1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -704,7 +725,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     bf16x8 pb[2];
     {
       f32x4 s0[4];
-      qk_tile(smem, s0, [](int) {}, [] {}, true);
+      qk_tile(smem, s0, [](int) {}, [](int) {}, true);
       const bool nm0 = kv0 + kTile > lim_wave;
 #pragma unroll
       for (int step = 0; step < kSoftmaxSteps; ++step) softmax_step(step, s0, nm0, kv0);
@@ -737,7 +758,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           if (decltype(ic)::value == i) dma(ic, nsrc, nbuf);
         });
       };
-      i16x8 v[DV + 1];
+      i16x4 v[DV + 1][2];
       f32x4 s_next[4];
       if (has_next) {
         // P of tile it (from the previous iteration's softmax) becomes the PV
@@ -748,11 +769,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
               if ((k & 15) == 4) copy_at(k >> 4);
               if (k == 10 || k == 26) pack_half(pb, k == 26);
             },
-            [&] { pv_prefetch(vb, v); }, false);
+            [&](int j) {
+              if (j < 2 * DV) pv_prefetch(vb, v, j);
+            },
+            false);
       } else {
         pack_p(pb);
         dma_all(nsrc, nbuf);
-        pv_prefetch(vb, v);
+#pragma unroll
+        for (int i = 0; i < 2 * DV; ++i) pv_prefetch(vb, v, i);
       }
       __builtin_amdgcn_sched_barrier(0);
 

@@ -11,7 +11,10 @@ kernel's comments promise:
   * the registers of the asynchronous query and page-id loads are not touched
     between the load and the first explicit vmcnt wait after it;
   * every vmcnt wait in the decode kernel is one the source writes explicitly
-    (the compiler adds none: an extra one would serialize the copy pipeline).
+    (the compiler adds none: an extra one would serialize the copy pipeline);
+  * no VALU instruction overwrites the data registers of a preceding store of
+    more than 8 bytes in the next wait state (gfx9-family store data hazard;
+    the asm stores carry their own s_nop).
 """
 from __future__ import annotations
 
@@ -130,6 +133,34 @@ def async_load_violations(body: list) -> list:
             if any(_regs(o) & dst for o in uops):
                 bad.append((t, u))
                 break
+    return bad
+
+
+def store_data_hazards(body: list, need: int = 1) -> list:
+    """(store, valu) pairs where VALU writes a 12/16-byte store's data registers too soon."""
+    bad = []
+    for i, t in enumerate(body):
+        op, ops = _split(t)
+        if not re.match(r"(global|buffer|flat)_store_dwordx[34]$", op) or len(ops) < 2:
+            continue
+        data = _regs(ops[1])
+        left, j = need, i + 1
+        while left > 0 and j < len(body):
+            uop, uops = _split(body[j])
+            if uop == "s_nop":
+                left -= int(uops[0], 0) + 1
+                j += 1
+                continue
+            if uop.startswith("v_") and uops:
+                written = _regs(uops[0])
+                if uop.startswith("v_permlane"):
+                    for o in uops[:2]:
+                        written |= _regs(o)
+                if written & data:
+                    bad.append((t, body[j]))
+                    break
+            left -= 1
+            j += 1
     return bad
 
 

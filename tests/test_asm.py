@@ -59,3 +59,12 @@ def test_only_explicit_vmcnt_waits(asm):
         waits = asm_checks.vmcnt_waits(body)
         counts = sorted({int(w.split("vmcnt(")[1].split(")")[0]) for w in waits})
         assert counts == [0, 9, 18, 36], waits
+
+
+def test_no_store_data_hazards(asm):
+    # every kernel of the library: the decode kernel's inline-asm stores and
+    # the compiler's own stores in the combine kernels
+    bodies = asm_checks.kernel_bodies(asm, prefix="_ZN3mla")
+    assert len(bodies) >= 4
+    for body in bodies:
+        assert asm_checks.store_data_hazards(body) == []
