@@ -69,6 +69,9 @@ SMALL = [
     (2, 64, 3, 128, [3, 400]),
     (5, 128, 1, 256, [1000, 1, 513, 64, 300]),
     (1, 32, 8, 16, [111]),
+    # full head count with long drafts: 4 and 8 row blocks of 128 rows per request
+    (3, 128, 4, 16, [1000, 257, 31]),
+    (2, 128, 8, 32, [700, 9]),
 ]
 
 
