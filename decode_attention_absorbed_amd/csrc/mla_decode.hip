@@ -19,10 +19,12 @@
 //    (all 32 rows of a chunk together) with the two row halves of odd chunks
 //    swapped, so that both the row reads of QK^T and the transposed reads of
 //    PV hit distinct banks (layout below);
-//  * all products are v_mfma_f32_16x16x32_bf16.  (The 32x32x16 form needs a
-//    36-step dependent chain per tile for QK^T, which runs at a third of the
-//    matrix rate; the 16x16 form gives four independent 18-step chains, and a
-//    K of 32 lets one PV product cover a whole tile.)
+//  * all products are v_mfma_f32_16x16x32_bf16: a K of 32 lets one PV
+//    product cover a whole tile, and two rows per lane keep the P^T operand
+//    in registers.  (A version on v_mfma_f32_32x32x16_bf16, with half the
+//    MFMA instructions and one row per lane, took 8% fewer cycles per tile,
+//    but the chip's clock under that load dropped by as much: measured, no
+//    net gain.)
 //  * wave w owns 32 query rows as two blocks of 16 (hb = 0, 1).  Its query
 //    rows stay in 144 VGPRs as the B operand for the whole piece.
 //    S^T = K Q^T for the tile: 2 key blocks x 2 row blocks; lane l holds rows
