@@ -9,6 +9,9 @@ nothing from ``decode_attention_absorbed_amd``.
 Every function here is pinned by the ``-m "not gpu"`` tests against
 something other than itself (brute force, closed forms, the unabsorbed
 multi-head form, scipy's softmax, invariants); none is "parity unpinned".
+The FP8 variant (``mla_oracle_fp8``) is pinned against the OCP E4M3/E8M0
+definitions, torch's float8_e4m3fn conversion and the bf16 reference on
+inputs whose quantization is exact (tests/test_oracle_fp8.py).
 """
 from .mla_oracle import (  # noqa: F401
     absorb_query,
@@ -20,4 +23,19 @@ from .mla_oracle import (  # noqa: F401
     mla_decode_ref,
     mla_decode_split_ref,
     visible_keys,
+)
+from .mla_oracle_fp8 import (  # noqa: F401
+    E4M3_MAX,
+    E4M3_REL_RMS,
+    dequantize_cache,
+    dequantize_query,
+    e4m3_decode,
+    e4m3_round,
+    e4m3_table,
+    e4m3_value,
+    e8m0_decode,
+    fp8_weight_error_rms,
+    mla_decode_fp8_ref,
+    query_exponent,
+    quantize_query,
 )

@@ -1,0 +1,233 @@
+"""Pins for the FP8 part of the oracle (CPU only).
+
+The E4M3 / E8M0 helpers are checked against the formats' published
+definitions and against torch's float8_e4m3fn conversion (a library routine
+that implements the same OCP format); the FP8 decode reference is checked
+against the (separately pinned) bf16 reference on inputs whose quantization is
+exact, with the dequantization done by another route; the weight-rounding
+error model is checked against a direct simulation of that rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (
+    E4M3_REL_RMS,
+    dequantize_cache,
+    dequantize_query,
+    e4m3_decode,
+    e4m3_round,
+    e4m3_table,
+    e8m0_decode,
+    fp8_weight_error_rms,
+    mla_decode_fp8_ref,
+    mla_decode_ref,
+    query_exponent,
+    quantize_query,
+)
+from workloads import bf16_bits_to_f64, make_inputs_fp8
+
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+def torch_e4m3_values() -> np.ndarray:
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def torch_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_table_matches_torch():
+    ours, ref = e4m3_table(), torch_e4m3_values()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_format_facts():
+    """Values the OCP FP8 definition fixes for the E4M3 encoding."""
+    v = e4m3_table()
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0  # largest finite magnitude
+    assert v[0x08] == 2.0**-6  # smallest normal
+    assert v[0x01] == 2.0**-9  # smallest subnormal
+    assert v[0x07] == 7 * 2.0**-9  # largest subnormal
+    assert v[0x38] == 1.0 and v[0x40] == 2.0 and v[0x3C] == 1.5
+    assert v[0x00] == 0.0 and np.signbit(v[0x80]) and v[0x80] == 0.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254  # no infinities, two NaN codes
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)  # codes 0x00..0x7E increase
+
+
+def _rounding_grid() -> np.ndarray:
+    pos = e4m3_table()[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    f32 = lambda a: np.asarray(a, np.float32)
+    near = np.concatenate(
+        [np.nextafter(f32(mids), f32(0)), np.nextafter(f32(mids), f32(1000)), f32(mids), f32(pos)]
+    ).astype(np.float64)
+    rng = np.random.default_rng(5)
+    rnd = np.concatenate([rng.standard_normal(4000) * 50, rng.uniform(-463.9, 463.9, 4000), rng.standard_normal(500) * 1e-3])
+    g = np.concatenate([near, rnd, [448.0, 463.9, 2.0**-10, 2.0**-11, 3 * 2.0**-11, 2.0**-12]])
+    g = np.concatenate([g, -g]).astype(np.float32).astype(np.float64)
+    return g[np.abs(g) < 464]
+
+
+def test_e4m3_round_matches_torch():
+    g = _rounding_grid()
+    assert np.array_equal(e4m3_round(g), torch_e4m3_codes(g))
+
+
+def test_e4m3_round_is_nearest_ties_even():
+    """Brute force: no finite code is closer; on a tie the code is even."""
+    rng = np.random.default_rng(6)
+    pos = e4m3_table()[:0x7F]
+    x = np.concatenate([rng.uniform(0, 463.9, 3000), (pos[:-1] + pos[1:]) / 2])
+    codes = e4m3_round(x)
+    vals = e4m3_decode(codes)
+    d_all = np.abs(x[:, None] - pos[None, :])
+    best = d_all.min(axis=1)
+    assert np.all(np.abs(x - vals) == best)
+    tie = (d_all == best[:, None]).sum(axis=1) == 2
+    assert tie.sum() >= 100 and np.all(codes[tie] % 2 == 0)
+    with pytest.raises(ValueError):
+        e4m3_round(np.array([464.0]))
+
+
+def test_e8m0_decode():
+    e = np.array([0, 1, 126, 127, 128, 200, 254, 255])
+    v = e8m0_decode(e)
+    assert v[3] == 1.0 and v[2] == 0.5 and v[4] == 2.0 and v[0] == 2.0**-127 and v[6] == 2.0**127
+    assert np.isnan(v[7])
+
+
+def test_query_exponent_definition():
+    """f is the smallest integer with amax * 2^-f <= 448: brute force."""
+    rng = np.random.default_rng(7)
+    cands = list(rng.uniform(0, 1, 300) * 10.0 ** rng.integers(-30, 30, 300))
+    for k in range(-20, 20):
+        for m in (448.0, np.nextafter(448.0, 0), np.nextafter(448.0, 1e9), 224.0, 300.0, 449.0):
+            cands.append(math.ldexp(float(m), k))
+    cands += [float(np.float32(1e-40)), 1e-3, 7.0]  # includes an fp32 subnormal
+    for a in cands:
+        f = query_exponent(a)
+        assert math.ldexp(a, -f) <= 448.0 < math.ldexp(a, -(f - 1)), (a, f)
+    assert query_exponent(0.0) == 0
+    assert query_exponent(448.0) == 0 and query_exponent(449.0) == 1 and query_exponent(224.0) == -1
+
+
+def test_query_quantization_matches_torch_rounding():
+    """Codes of real query rows: torch's conversion of q * 2^-f in float32
+    (the scaling by 2^-f is exact in float32 for these rows)."""
+    x = make_inputs_fp8(2, 8, 2, 16, [40, 70], seed=31)
+    qn, qp = x.q_nope_f64(), x.q_pe_f64()
+    codes, f = quantize_query(qn, qp)
+    q = np.concatenate([qn, qp], axis=-1)
+    scaled = np.ldexp(q, -f[..., None]).astype(np.float32)
+    assert np.array_equal(scaled.astype(np.float64), np.ldexp(q, -f[..., None]))
+    assert np.array_equal(codes, torch_e4m3_codes(scaled))
+    # every row uses its range: amax * 2^-f is in (224, 448], so the largest
+    # code (after rounding, whose step is 32 there) is in [224, 448]
+    mag = np.abs(e4m3_decode(codes)).max(axis=-1)
+    assert np.all(mag >= 224) and np.all(mag <= 448)
+    # dequantized within half a step (relative 2^-4) of the query for normal codes
+    dq = dequantize_query(codes, f)
+    big = np.abs(scaled) >= 2.0**-6
+    assert np.all(np.abs(dq - q)[big] <= 2.0**-4 * np.abs(q)[big])
+
+
+def _exact_inputs(seed=41, batch=2, heads=4, q_len=2, page=8, lens=(13, 29)):
+    """FP8 inputs plus queries that quantize exactly: every query row is made
+    of E4M3 values times 2^g, and its largest magnitude is 448 * 2^g."""
+    x = make_inputs_fp8(batch, heads, q_len, page, list(lens), seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    pos = e4m3_table()[:0x7F]
+    vals = rng.choice(pos[pos > 0], size=(batch, q_len, heads, 576)) * rng.choice([-1.0, 1.0], size=(batch, q_len, heads, 576))
+    g = rng.integers(-12, -4, size=(batch, q_len, heads))
+    idx = rng.integers(0, 576, size=(batch, q_len, heads))
+    np.put_along_axis(vals, idx[..., None], 448.0, axis=-1)
+    q = np.ldexp(vals, g[..., None])
+    return x, q[..., :512], q[..., 512:], g
+
+
+def test_fp8_reference_reduces_to_bf16_reference():
+    x, qn, qp, g = _exact_inputs()
+    codes, f = quantize_query(qn, qp)
+    assert np.array_equal(f, g)
+    assert np.array_equal(dequantize_query(codes, f), np.concatenate([qn, qp], axis=-1))
+    # the cache dequantized by another route: torch's decode of the codes
+    # times 2^(e - 127) via ldexp
+    dec = torch.from_numpy(x.cache_codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    cache = np.ldexp(dec, x.cache_exps.astype(np.int64)[..., None] - 127)
+    assert np.array_equal(cache, dequantize_cache(x.cache_codes, x.cache_exps))
+    out8, lse8 = mla_decode_fp8_ref(qn, qp, x.cache_codes, x.cache_exps, x.block_table, x.seq_lens, SCALE)
+    out, lse = mla_decode_ref(qn, qp, cache, x.block_table, x.seq_lens, SCALE)
+    np.testing.assert_allclose(out8, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse8, lse, rtol=0, atol=1e-12)
+
+
+def test_fp8_reference_uses_token_scales():
+    """Doubling one token's scale byte doubles its row: the result must equal
+    the bf16 reference on the doubled row (and differ from the original)."""
+    x, qn, qp, _ = _exact_inputs(seed=43)
+    out0, _ = mla_decode_fp8_ref(qn, qp, x.cache_codes, x.cache_exps, x.block_table, x.seq_lens, SCALE)
+    exps = x.cache_exps.copy()
+    p0 = int(x.block_table[0, 0])
+    exps[p0, 3] += 1
+    out1, lse1 = mla_decode_fp8_ref(qn, qp, x.cache_codes, exps, x.block_table, x.seq_lens, SCALE)
+    cache = dequantize_cache(x.cache_codes, x.cache_exps)
+    cache[p0, 3] *= 2.0
+    out, lse = mla_decode_ref(qn, qp, cache, x.block_table, x.seq_lens, SCALE)
+    np.testing.assert_allclose(out1, out, rtol=0, atol=1e-12)
+    assert np.abs(out1[0] - out0[0]).max() > 1e-3
+
+
+def test_weight_error_model_against_simulation():
+    """Round the exact softmax weights as the model describes (scaled so the
+    row's largest weight sits at 2^(6 + d) for the largest-scale token, d
+    uniform in [0, 2) per row like a reference that trails the row maximum,
+    E4M3 round-to-nearest), and compare the resulting output error with the
+    model's root-mean-square prediction."""
+    x = make_inputs_fp8(2, 8, 1, 16, [300, 700], seed=51)
+    qn, qp = x.q_nope_f64(), x.q_pe_f64()
+    pred = fp8_weight_error_rms(qn, qp, x.cache_codes, x.cache_exps, x.block_table, x.seq_lens, SCALE)
+    codes, f = quantize_query(qn, qp)
+    q = dequantize_query(codes, f)
+    cache = dequantize_cache(x.cache_codes, x.cache_exps)
+    ratios = []
+    for b in range(2):
+        L = int(x.seq_lens[b])
+        t = np.arange(L)
+        pages = x.block_table[b, t // 16]
+        K = cache[pages, t % 16]
+        e = x.cache_exps[pages, t % 16].astype(np.int64)
+        s = SCALE * (q[b, 0] @ K.T)
+        w = np.exp(s - s.max(axis=-1, keepdims=True))
+        w /= w.sum(axis=-1, keepdims=True)
+        wmax = w.max(axis=-1, keepdims=True)
+        d = np.random.default_rng(52 + b).uniform(0, 2, size=(wmax.shape[0], 1))
+        sc = np.ldexp(1.0, 6 + e - e.max())[None, :] * 2.0**d / wmax
+        w_r = e4m3_decode(e4m3_round(w * sc)) / sc
+        err = (w_r - w) @ K[:, :512]
+        ratios.append(np.sqrt((err**2).sum()) / np.sqrt((pred[b, 0] ** 2).sum()))
+    # the model is an estimate of the same quantity: same order, not vacuous
+    assert all(0.4 < r < 1.6 for r in ratios), ratios
+    assert E4M3_REL_RMS == pytest.approx(2.0**-4 / math.sqrt(3.0))
+
+
+def test_fp8_generator_ranges():
+    x = make_inputs_fp8(2, 4, 1, 16, [37, 100], seed=61)
+    v = e4m3_decode(x.cache_codes)
+    assert np.isfinite(v).all() and np.abs(v).max() <= 448
+    assert x.cache_exps.min() >= 119 and x.cache_exps.max() <= 123
+    # the same layout and queries as the bf16 recipe with the same seed
+    from workloads import make_inputs
+
+    y = make_inputs(2, 4, 1, 16, [37, 100], seed=61)
+    assert np.array_equal(x.block_table, y.block_table) and np.array_equal(x.q_nope, y.q_nope)
+    assert np.array_equal(bf16_bits_to_f64(x.q_pe), y.q_pe_f64())

@@ -151,27 +151,7 @@ def make_inputs(
     contents are drawn too, and callers may poison them).
     """
     rng = np.random.default_rng(seed)
-    if isinstance(lens, tuple) and lens and lens[0] == "uniform":
-        _, lo, hi = lens
-        base = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
-    else:
-        base = np.asarray(list(lens), dtype=np.int64)
-        if base.shape[0] != batch:
-            raise ValueError("len(lens) must equal batch")
-    order = rng.permutation(batch)
-    seq_lens = base[order].astype(np.int32)
-
-    npg = pages_needed(seq_lens, page)
-    used = int(sum(npg))
-    num_pages = used + int(extra_pages)
-    perm = rng.permutation(used).astype(np.int32)
-    bt_stride = max(1, max(npg) if npg else 1)
-    block_table = np.full((batch, bt_stride), -1, dtype=np.int32)
-    off = 0
-    for b, n in enumerate(npg):
-        block_table[b, :n] = perm[off : off + n]
-        off += n
-
+    seq_lens, block_table, num_pages = _draw_layout(rng, batch, page, lens, extra_pages)
     if draw_values:
         q_nope = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_LATENT), dtype=np.float32))
         q_pe = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_ROPE), dtype=np.float32))
@@ -193,6 +173,31 @@ def make_inputs(
         q_pe=q_pe,
         cache=cache,
     )
+
+
+def _draw_layout(rng, batch: int, page: int, lens, extra_pages: int):
+    """Steps 1-3 of the recipe: lengths, request order, page permutation."""
+    if isinstance(lens, tuple) and lens and lens[0] == "uniform":
+        _, lo, hi = lens
+        base = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
+    else:
+        base = np.asarray(list(lens), dtype=np.int64)
+        if base.shape[0] != batch:
+            raise ValueError("len(lens) must equal batch")
+    order = rng.permutation(batch)
+    seq_lens = base[order].astype(np.int32)
+
+    npg = pages_needed(seq_lens, page)
+    used = int(sum(npg))
+    num_pages = used + int(extra_pages)
+    perm = rng.permutation(used).astype(np.int32)
+    bt_stride = max(1, max(npg) if npg else 1)
+    block_table = np.full((batch, bt_stride), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npg):
+        block_table[b, :n] = perm[off : off + n]
+        off += n
+    return seq_lens, block_table, num_pages
 
 
 def make_config(name: str, seed: Optional[int] = None) -> MLAInputs:
@@ -233,3 +238,124 @@ def poison_unreferenced(x: MLAInputs, value_bits: int = 0x7FC0) -> None:
         n = -(-int(x.seq_lens[b]) // x.page)
         ref[x.block_table[b, :n]] = True
     x.cache[~ref] = value_bits
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache
+# ---------------------------------------------------------------------------
+#: Cache values are drawn as N(0, 1) and stored as E4M3 codes of 64 x (so the
+#: largest |x| the draw keeps, 7, maps to 448); the token's E8M0 scale byte is
+#: 121 + k with k uniform in {-2, ..., 2}, so token t's row is about 2^k x:
+#: token magnitudes spread over a factor 16, as a per-token scale is there for.
+FP8_CODE_GAIN = 64.0
+FP8_CLIP = 7.0
+FP8_EXP_CENTER = 121
+FP8_EXP_SPREAD = 2
+
+
+@dataclass
+class MLAInputsFP8:
+    """One batch of decode inputs over an FP8 cache (queries as bf16 bits)."""
+
+    name: str
+    batch: int
+    heads: int
+    q_len: int
+    page: int
+    seq_lens: np.ndarray  # int32 [B]
+    block_table: np.ndarray  # int32 [B, bt_stride], -1 padded
+    num_pages: int
+    q_nope: np.ndarray  # uint16 [B, q_len, H, 512]
+    q_pe: np.ndarray  # uint16 [B, q_len, H, 64]
+    cache_codes: np.ndarray  # uint8 [num_pages, page, 576], E4M3
+    cache_exps: np.ndarray  # uint8 [num_pages, page], E8M0
+    softmax_scale: float = field(default_factory=softmax_scale_default)
+
+    @property
+    def bt_stride(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def q_nope_f64(self) -> np.ndarray:
+        return bf16_bits_to_f64(self.q_nope)
+
+    def q_pe_f64(self) -> np.ndarray:
+        return bf16_bits_to_f64(self.q_pe)
+
+    def to_torch(self, device: str = "cpu") -> dict:
+        """Torch tensors of the same bits for the HIP path."""
+        import torch
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+        return dict(
+            q_nope=bf16(self.q_nope),
+            q_pe=bf16(self.q_pe),
+            cache_codes=torch.from_numpy(np.ascontiguousarray(self.cache_codes)).to(device),
+            cache_exps=torch.from_numpy(np.ascontiguousarray(self.cache_exps)).to(device),
+            block_table=torch.from_numpy(np.ascontiguousarray(self.block_table)).to(device),
+            seq_lens=torch.from_numpy(np.ascontiguousarray(self.seq_lens)).to(device),
+        )
+
+
+def e4m3_codes_of(x: np.ndarray) -> np.ndarray:
+    """E4M3 codes of float32 values via torch's float8_e4m3fn conversion (a
+    library routine; |x| must stay within 448)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def make_inputs_fp8(
+    batch: int,
+    heads: int,
+    q_len: int,
+    page: int,
+    lens: Sequence[int] | tuple,
+    seed: int,
+    name: str = "custom",
+    extra_pages: int = 0,
+) -> MLAInputsFP8:
+    """Draw one seeded FP8 batch: steps 1-5 of the bf16 recipe (lengths,
+    order, pages, q_nope, q_pe), then 6. cache values N(0, 1) float32, clipped
+    to +-FP8_CLIP and stored as codes of FP8_CODE_GAIN * x, 7. per-token scale
+    bytes FP8_EXP_CENTER + k, k uniform in [-FP8_EXP_SPREAD, FP8_EXP_SPREAD]."""
+    rng = np.random.default_rng(seed)
+    seq_lens, block_table, num_pages = _draw_layout(rng, batch, page, lens, extra_pages)
+    q_nope = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_LATENT), dtype=np.float32))
+    q_pe = to_bf16_bits(rng.standard_normal((batch, q_len, heads, D_ROPE), dtype=np.float32))
+    x = rng.standard_normal((num_pages, page, D_QK), dtype=np.float32)
+    np.clip(x, -FP8_CLIP, FP8_CLIP, out=x)
+    x *= np.float32(FP8_CODE_GAIN)
+    codes = e4m3_codes_of(x)
+    k = rng.integers(-FP8_EXP_SPREAD, FP8_EXP_SPREAD + 1, size=(num_pages, page))
+    exps = (FP8_EXP_CENTER + k).astype(np.uint8)
+    return MLAInputsFP8(
+        name=name,
+        batch=batch,
+        heads=heads,
+        q_len=q_len,
+        page=page,
+        seq_lens=seq_lens,
+        block_table=block_table,
+        num_pages=num_pages,
+        q_nope=q_nope,
+        q_pe=q_pe,
+        cache_codes=codes,
+        cache_exps=exps,
+    )
+
+
+def make_config_fp8(name: str, seed: Optional[int] = None) -> MLAInputsFP8:
+    """A named workload's shapes and seed with an FP8 cache."""
+    c = CONFIGS[name]
+    return make_inputs_fp8(
+        batch=c["batch"],
+        heads=c["heads"],
+        q_len=c["q_len"],
+        page=c["page"],
+        lens=c["lens"],
+        seed=c["seed"] if seed is None else seed,
+        name=name,
+    )
