@@ -14,12 +14,14 @@ below is a reading, listed with the others in the design notes:
     finite magnitude 448) and one scale exponent byte e_t in the OCP MX E8M0
     encoding (value 2^(e_t - 127), 255 is NaN).  The token's row is
         K_t = 2^(e_t - 127) * decode(codes_t),   V_t = K_t[0:512];
-  * queries arrive in bf16, as in the bf16 path, and are quantized per row
-    (one (request, query token, head) row of 576 values): the row's exponent
-    f is the smallest integer with amax * 2^-f <= 448 (f = 0 for a zero row)
-    and its codes are the nearest E4M3 values of q * 2^-f (ties to the even
-    code).  Scaling by a power of two is exact, so the only rounding is the
-    final one;
+  * queries arrive in bf16, as in the bf16 path, and are quantized in the
+    OCP MXFP8 way: each block of 32 consecutive values of a (request, query
+    token, head) row of 576 gets its own exponent f, the smallest integer
+    with amax * 2^-f <= 448 (f = 0 for a zero block), limited to the E8M0
+    range [-127, 127]; its codes are the nearest E4M3 values of q * 2^-f
+    (ties to the even code; limiting f from below keeps the block under 448,
+    and bf16 cannot reach the upper limit).  Scaling by a power of two is
+    exact, so the only rounding is the final one;
   * attention is then the definition of the bf16 path applied to the
     dequantized rows, in fp64: s_t = scale * (q_deq . K_t), lse = log sum
     exp s_t, out = sum_t exp(s_t - lse) V_t.
@@ -126,26 +128,34 @@ def query_exponent(amax: float) -> int:
     return f
 
 
+#: values per query block sharing one exponent (the OCP MX block size)
+MX_BLOCK = 32
+
+
 def quantize_query(q_nope: np.ndarray, q_pe: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per-row E4M3 quantization of the queries.
+    """MXFP8 quantization of the queries.
 
     q_nope [..., 512] and q_pe [..., 64] (float64 holding bf16 values).
-    Returns (codes [..., 576] uint8, f [...] int64) with q ~= decode(codes) * 2^f.
+    Returns (codes [..., 576] uint8, f [..., 18] int64): value k of a row is
+    about decode(codes[k]) * 2^f[k // 32].
     """
     q = np.concatenate([np.asarray(q_nope, np.float64), np.asarray(q_pe, np.float64)], axis=-1)
     lead = q.shape[:-1]
-    flat = q.reshape(-1, D_QK)
-    codes = np.zeros(flat.shape, dtype=np.uint8)
-    f = np.zeros(flat.shape[0], dtype=np.int64)
-    for r in range(flat.shape[0]):
-        f[r] = query_exponent(np.abs(flat[r]).max())
-        codes[r] = e4m3_round(np.ldexp(flat[r], -int(f[r])))
-    return codes.reshape(lead + (D_QK,)), f.reshape(lead)
+    nb = D_QK // MX_BLOCK
+    blocks = q.reshape(-1, nb, MX_BLOCK)
+    codes = np.zeros(blocks.shape, dtype=np.uint8)
+    f = np.zeros(blocks.shape[:2], dtype=np.int64)
+    for r in range(blocks.shape[0]):
+        for k in range(nb):
+            fb = min(max(query_exponent(np.abs(blocks[r, k]).max()), -127), 127)
+            f[r, k] = fb
+            codes[r, k] = e4m3_round(np.clip(np.ldexp(blocks[r, k], -fb), -E4M3_MAX, E4M3_MAX))
+    return codes.reshape(lead + (D_QK,)), f.reshape(lead + (nb,))
 
 
 def dequantize_query(codes: np.ndarray, f: np.ndarray) -> np.ndarray:
-    """decode(codes) * 2^f, float64 [..., 576]."""
-    return np.ldexp(e4m3_decode(codes), np.asarray(f, np.int64)[..., None])
+    """decode(codes) * 2^f per block, float64 [..., 576]."""
+    return np.ldexp(e4m3_decode(codes), np.repeat(np.asarray(f, np.int64), MX_BLOCK, axis=-1))
 
 
 def dequantize_cache(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:

@@ -122,36 +122,62 @@ def test_query_exponent_definition():
 
 
 def test_query_quantization_matches_torch_rounding():
-    """Codes of real query rows: torch's conversion of q * 2^-f in float32
-    (the scaling by 2^-f is exact in float32 for these rows)."""
+    """Codes of real query rows: torch's conversion of q * 2^-f in float32,
+    f per block of 32 (the scaling by 2^-f is exact in float32 here)."""
     x = make_inputs_fp8(2, 8, 2, 16, [40, 70], seed=31)
     qn, qp = x.q_nope_f64(), x.q_pe_f64()
     codes, f = quantize_query(qn, qp)
+    assert f.shape == (2, 2, 8, 18)
     q = np.concatenate([qn, qp], axis=-1)
-    scaled = np.ldexp(q, -f[..., None]).astype(np.float32)
-    assert np.array_equal(scaled.astype(np.float64), np.ldexp(q, -f[..., None]))
+    fe = np.repeat(f, 32, axis=-1)
+    scaled = np.ldexp(q, -fe).astype(np.float32)
+    assert np.array_equal(scaled.astype(np.float64), np.ldexp(q, -fe))
     assert np.array_equal(codes, torch_e4m3_codes(scaled))
-    # every row uses its range: amax * 2^-f is in (224, 448], so the largest
+    # every block uses its range: amax * 2^-f is in (224, 448], so its largest
     # code (after rounding, whose step is 32 there) is in [224, 448]
-    mag = np.abs(e4m3_decode(codes)).max(axis=-1)
+    mag = np.abs(e4m3_decode(codes)).reshape(2, 2, 8, 18, 32).max(axis=-1)
     assert np.all(mag >= 224) and np.all(mag <= 448)
     # dequantized within half a step (relative 2^-4) of the query for normal codes
     dq = dequantize_query(codes, f)
     big = np.abs(scaled) >= 2.0**-6
     assert np.all(np.abs(dq - q)[big] <= 2.0**-4 * np.abs(q)[big])
+    # blocks are independent: scaling one block of one row by 2^5 moves only
+    # that block's exponent
+    qn2 = qn.copy()
+    qn2[0, 0, 0, 64:96] *= 32.0
+    codes2, f2 = quantize_query(qn2, qp)
+    assert f2[0, 0, 0, 2] == f[0, 0, 0, 2] + 5
+    f2[0, 0, 0, 2] -= 5
+    assert np.array_equal(f2, f) and np.array_equal(codes2, codes)
+
+
+def test_query_quantization_limits():
+    """Exponents below the E8M0 range are limited to -127 (the block then
+    stays below 448, so nothing saturates); zero blocks take f = 0."""
+    qn = np.zeros((1, 1, 1, 512))
+    qp = np.zeros((1, 1, 1, 64))
+    qn[..., 0:32] = 2.0**-130  # would need f = -138: limited to -127, 2^-3 scaled
+    qn[..., 32] = 2.0**-118  # f = -126: 2^8
+    qn[..., 64] = 3.0  # f = -7: 384
+    codes, f = quantize_query(qn, qp)
+    assert f[0, 0, 0, 0] == -127 and f[0, 0, 0, 1] == -126 and f[0, 0, 0, 2] == -7 and f[0, 0, 0, 3] == 0
+    assert e4m3_decode(codes[0, 0, 0, 0:1])[0] == 2.0**-3
+    assert e4m3_decode(codes[0, 0, 0, 32:33])[0] == 256.0
+    assert e4m3_decode(codes[0, 0, 0, 64:65])[0] == 384.0
 
 
 def _exact_inputs(seed=41, batch=2, heads=4, q_len=2, page=8, lens=(13, 29)):
-    """FP8 inputs plus queries that quantize exactly: every query row is made
-    of E4M3 values times 2^g, and its largest magnitude is 448 * 2^g."""
+    """FP8 inputs plus queries that quantize exactly: every block of 32 of a
+    query row is made of E4M3 values times 2^g, with largest magnitude 448 * 2^g."""
     x = make_inputs_fp8(batch, heads, q_len, page, list(lens), seed=seed)
     rng = np.random.default_rng(seed + 1)
     pos = e4m3_table()[:0x7F]
-    vals = rng.choice(pos[pos > 0], size=(batch, q_len, heads, 576)) * rng.choice([-1.0, 1.0], size=(batch, q_len, heads, 576))
-    g = rng.integers(-12, -4, size=(batch, q_len, heads))
-    idx = rng.integers(0, 576, size=(batch, q_len, heads))
+    shape = (batch, q_len, heads, 18, 32)
+    vals = rng.choice(pos[pos > 0], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+    g = rng.integers(-12, -4, size=shape[:-1])
+    idx = rng.integers(0, 32, size=shape[:-1])
     np.put_along_axis(vals, idx[..., None], 448.0, axis=-1)
-    q = np.ldexp(vals, g[..., None])
+    q = np.ldexp(vals, g[..., None]).reshape(batch, q_len, heads, 576)
     return x, q[..., :512], q[..., 512:], g
 
 
