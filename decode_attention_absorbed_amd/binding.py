@@ -46,6 +46,10 @@ EXPORTED = (
     "mla_last_error",
     "mla_plan_query",
     "mla_plan_copy",
+    "mla_decode_fp8_plan",
+    "mla_decode_fp8_plan_host",
+    "mla_decode_fp8",
+    "mla_decode_fp8_partials",
 )
 
 
@@ -97,6 +101,16 @@ def lib() -> ctypes.CDLL:
     L.mla_plan_query.restype = ctypes.c_int64
     L.mla_plan_copy.argtypes = [vp, i32p, i32p]
     L.mla_plan_copy.restype = ctypes.c_int
+    L.mla_decode_fp8_plan.argtypes = L.mla_decode_plan.argtypes
+    L.mla_decode_fp8_plan.restype = ctypes.c_int
+    L.mla_decode_fp8_plan_host.argtypes = L.mla_decode_plan.argtypes
+    L.mla_decode_fp8_plan_host.restype = ctypes.c_int
+    L.mla_decode_fp8.argtypes = [
+        vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp,
+    ]
+    L.mla_decode_fp8.restype = ctypes.c_int
+    L.mla_decode_fp8_partials.argtypes = L.mla_decode_fp8.argtypes
+    L.mla_decode_fp8_partials.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -160,7 +174,7 @@ def _make_plan(fn_name: str, seq_lens: Sequence[int], q_len: int, num_heads: int
     h = ctypes.c_void_p()
     fn = getattr(lib(), fn_name)
     _check(fn(lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(lens.shape[0]), int(q_len), int(num_heads), int(page_size), int(num_cus), ctypes.byref(h)))
-    return Plan(h.value, lens, q_len, num_heads, page_size, fn_name == "mla_decode_plan")
+    return Plan(h.value, lens, q_len, num_heads, page_size, fn_name in ("mla_decode_plan", "mla_decode_fp8_plan"))
 
 
 def mla_decode_plan(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int = 0) -> Plan:
@@ -171,6 +185,16 @@ def mla_decode_plan(seq_lens: Sequence[int], q_len: int, num_heads: int, page_si
 def mla_decode_plan_host(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int) -> Plan:
     """Host-only plan (no HIP call): for inspection and argument checks."""
     return _make_plan("mla_decode_plan_host", seq_lens, q_len, num_heads, page_size, num_cus)
+
+
+def mla_decode_fp8_plan(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int = 0) -> Plan:
+    """Plan for the FP8-cache decode (64-key tiles; uploads the schedule)."""
+    return _make_plan("mla_decode_fp8_plan", seq_lens, q_len, num_heads, page_size, num_cus)
+
+
+def mla_decode_fp8_plan_host(seq_lens: Sequence[int], q_len: int, num_heads: int, page_size: int, num_cus: int) -> Plan:
+    """Host-only FP8 plan (no HIP call)."""
+    return _make_plan("mla_decode_fp8_plan_host", seq_lens, q_len, num_heads, page_size, num_cus)
 
 
 def mla_decode_workspace_bytes(plan: Plan) -> int:
@@ -236,6 +260,71 @@ def mla_decode(
             _ptr(q_pe),
             _ptr(kv_cache),
             int(kv_cache.shape[0]),
+            _ptr(block_table),
+            int(block_table.shape[1]),
+            _ptr(seq_lens),
+            float(softmax_scale),
+            _ptr(out),
+            _ptr(lse),
+            _ptr(workspace),
+            int(ws_bytes),
+            stream.cuda_stream,
+        )
+    )
+    return out, lse
+
+
+def mla_decode_fp8(
+    plan: Plan,
+    q_nope_absorbed: torch.Tensor,
+    q_pe: torch.Tensor,
+    kv_codes: torch.Tensor,
+    kv_scales: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    softmax_scale: float,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+    partials_only: bool = False,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue the FP8-cache decode (E4M3 codes [num_pages, page, 576] uint8 and
+    E8M0 token scales [num_pages, page] uint8); returns (out, lse).  With
+    ``partials_only`` only the decode kernel runs (mla_decode_fp8_partials)."""
+    B, qlen, H = plan.batch, plan.q_len, plan.num_heads
+    dev = q_nope_absorbed.device
+    _expect(q_nope_absorbed, "q_nope_absorbed", torch.bfloat16, (B, qlen, H, 512))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, qlen, H, 64))
+    if kv_codes.dim() != 3 or kv_codes.shape[1] != plan.page_size or kv_codes.shape[2] != 576:
+        raise ValueError(f"kv_codes: shape {tuple(kv_codes.shape)}, expected [num_pages, {plan.page_size}, 576]")
+    _expect(kv_codes, "kv_codes", torch.uint8, tuple(kv_codes.shape))
+    _expect(kv_scales, "kv_scales", torch.uint8, tuple(kv_codes.shape[:2]))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table: shape {tuple(block_table.shape)}, expected [{B}, *]")
+    _expect(block_table, "block_table", torch.int32, tuple(block_table.shape))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, qlen, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, qlen, H), dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, (B, qlen, H, 512))
+    _expect(lse, "lse", torch.float32, (B, qlen, H))
+    need = plan.workspace_bytes
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    fn = lib().mla_decode_fp8_partials if partials_only else lib().mla_decode_fp8
+    _check(
+        fn(
+            plan.handle,
+            _ptr(q_nope_absorbed),
+            _ptr(q_pe),
+            _ptr(kv_codes),
+            _ptr(kv_scales),
+            int(kv_codes.shape[0]),
             _ptr(block_table),
             int(block_table.shape[1]),
             _ptr(seq_lens),

@@ -51,19 +51,14 @@
 #include <string>
 #include <utility>
 
+#include "decode_fp8.h"
 #include "mla_decode.h"
 #include "plan_internal.h"
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS(T, p) ((__attribute__((address_space(3))) T*)(p))
+#include "device_common.h"
 
 constexpr int kRowBytes = 576 * 2;  // one cached token (HBM and LDS)
 constexpr int kChunks = 72;         // 16-byte chunks per cached token
@@ -107,90 +102,6 @@ static_assert(kLoadsPerWave - 5 + kSoftmaxSteps == 32, "PV gaps: 4 copies, then 
 //  * PV's transposed reads take 8 rows x 2 chunks per half wave (8 bytes per
 //    lane, 256 bytes per half wave), again in distinct banks.
 
-// Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
-// permlaneX_swap(x, x) returns the pair {x[l & ~X], x[l | X]} in some order,
-// so combining its two results is symmetric in the pair.
-// max of three floats in one instruction (the compiler's fmaxf adds NaN
-// canonicalization around every operand; v_max3_f32 treats NaN like fmaxf).
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ float group_max32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float group_max16(float x) {
-  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max3(__uint_as_float(s[0]), __uint_as_float(s[1]), __uint_as_float(s[1]));
-}
-
-__device__ __forceinline__ float group_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (N is an immediate).  The query loads and LDS copies are inline asm the
-// compiler does not count, so every wait on them is explicit.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16-byte global -> LDS copies (global_load_lds_dwordx4).  Each lane names its
-// own source; the 64 lanes of the wave fill 1 KB of LDS starting at M0.  They
-// are issued as inline asm on purpose: the compiler's wait-count pass treats a
-// pending LDS copy as aliasing every later LDS read and would insert
-// s_waitcnt vmcnt(0) before them, serializing the copy of later tiles with the
-// compute on this one.  (s_nop 0: one wait state between the M0 write and the
-// copy that reads it.)
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
-}
-
-// Same with a 64-bit per-lane address plus an immediate byte offset.  The
-// immediate offset moves the LDS destination too (lane l writes LDS byte
-// M0 + OFF + 16 l), so callers pass M0 = destination - OFF.
-template <int OFF>
-__device__ __forceinline__ void dma16_off(const void* src, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "{m0}"(lds_dst), "n"(OFF) : "memory");
-}
-
-// Same with a uniform base, a 32-bit per-lane offset and an immediate offset
-// (which, as above, is added to the LDS destination as well).
-template <int OFF>
-__device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, uint32_t lds_dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(off), "s"(base), "{m0}"(lds_dst), "n"(OFF)
-               : "memory");
-}
-
-// 4-byte global load into a VGPR, invisible to the compiler's wait counts
-// (waited for explicitly).
-__device__ __forceinline__ int load4(const int32_t* src) {
-  int v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(src) : "memory");
-  return v;
-}
-
-// 16-byte global load into VGPRs, invisible to the compiler's wait counts
-// (the explicit wait before the first QK^T covers it).
-__device__ __forceinline__ bf16x8 load16(const void* src) {
-  bf16x8 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
-  return v;
-}
-
 // The S^T accumulators are pinned to VGPRs (the softmax reads them with VALU
 // right away) while the output accumulators live in AGPRs; the compiler left to
 // itself puts both in AGPRs and spills.  So the QK^T MFMA is issued as inline
@@ -232,17 +143,6 @@ template <int N>
 __device__ __forceinline__ void o_set(float x);
 #include "agpr_tiles.inc"
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: loop bodies whose
-// register names must be compile-time constants.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Zero all 256 accumulators (start of a piece).
 template <int R>
 __device__ __forceinline__ void o_zero_rec() {
@@ -267,20 +167,6 @@ __device__ __forceinline__ void o_scale_all(float alpha0, float alpha1) { o_scal
 // Wait out the MFMA write -> AGPR read latency before reading results.
 __device__ __forceinline__ void o_drain() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
 
-// 16-byte store that writes through this XCD's L2 (system-scope coherence
-// bits): the kernel's results are read by the next kernel anyway, and lines
-// left dirty in L2 would all be written back at the end of the kernel, after
-// the last workgroup, instead of while the other workgroups still run.  A
-// store of more than 8 bytes reads its data registers after issue, so no VALU
-// instruction may overwrite them in the next wait state; the compiler does not
-// see this store, hence the s_nop (checked on the assembly).
-template <typename V>
-__device__ __forceinline__ void store_wt(void* p, const V& v) {
-  static_assert(sizeof(V) == 16, "one 16-byte store");
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(__builtin_bit_cast(u32x4, v))
-               : "memory");
-}
 
 // Store the 32 blocks of row block HB, scaled: block (cb, HB) goes to
 // dst[16cb .. 16cb+3] (dst already points at this lane's 4 columns).
@@ -1041,7 +927,7 @@ mla_status hip_fail(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
-                     int32_t page_size, int32_t num_cus, mla_plan** plan_out, bool upload) {
+                     int32_t page_size, int32_t num_cus, mla_plan** plan_out, bool upload, int32_t variant = 1) {
   if (!plan_out) return fail(MLA_ERR_INVALID_ARGUMENT, "plan_out is NULL");
   *plan_out = nullptr;
   if (!seq_lens_host) return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens_host is NULL");
@@ -1060,8 +946,9 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
   std::string err;
   int rc;
   try {
-    rc = mla::build_plan(seq_lens_host, batch, q_len, num_heads, page_size, num_cus, mla::PlanTuning{}, &p->d,
-                         &err);
+    mla::PlanTuning tuning;
+    tuning.variant = variant;
+    rc = mla::build_plan(seq_lens_host, batch, q_len, num_heads, page_size, num_cus, tuning, &p->d, &err);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(MLA_ERR_OUT_OF_MEMORY, "host allocation failed while planning");
@@ -1264,7 +1151,8 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;
   const bool single = d.page >= d.v.tile_tokens;
-  if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile) return fail(MLA_ERR_UNSUPPORTED, "plan variant has no kernel");
+  if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "plan was not made by mla_decode_plan (an FP8 plan runs with mla_decode_fp8)");
   hipError_t e = single ? launch_decode<true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
                                                  seq_lens, scale_log2, out, lse, ws, st)
                         : launch_decode<false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
@@ -1301,6 +1189,64 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void
   }
   g_last_error.clear();
   return MLA_OK;
+}
+
+mla_status mla_decode_fp8_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
+                               int32_t page_size, int32_t num_cus, mla_plan** plan_out) {
+  return make_plan(seq_lens_host, batch, q_len, num_heads, page_size, num_cus, plan_out, true, 2);
+}
+
+mla_status mla_decode_fp8_plan_host(const int32_t* seq_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
+                                    int32_t page_size, int32_t num_cus, mla_plan** plan_out) {
+  return make_plan(seq_lens_host, batch, q_len, num_heads, page_size, num_cus, plan_out, false, 2);
+}
+
+mla_status mla_decode_fp8_partials(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
+                                   const void* kv_codes, const void* kv_scales, int64_t num_pages,
+                                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                   float softmax_scale, float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!q_nope_absorbed || !q_pe || !kv_codes || !kv_scales || !block_table || !seq_lens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (!aligned(q_nope_absorbed, 16) || !aligned(q_pe, 16) || !aligned(kv_codes, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_nope_absorbed, q_pe, kv_codes and out must be 16-byte aligned");
+  if (!aligned(kv_scales, 4) || !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_scales, lse, block_table and seq_lens must be 4-byte aligned");
+  if (num_pages <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be > 0");
+  const mla::PlanData& d = plan->d;
+  if (d.v.tile_tokens != mla::kFp8TileTokens || d.v.waves != mla::kFp8Waves)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "plan was not made by mla_decode_fp8_plan");
+  if (bt_stride < d.max_pages)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "bt_stride (" + std::to_string(bt_stride) +
+                                              ") is smaller than the longest request's page count (" +
+                                              std::to_string(d.max_pages) + ")");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  Workspace ws;
+  mla_status st_ws = check_workspace(plan, workspace, workspace_bytes, &ws);
+  if (st_ws != MLA_OK) return st_ws;
+  mla_status st_dev = check_device(plan);
+  if (st_dev != MLA_OK) return st_dev;
+  const float scale_log2 = softmax_scale * 1.44269504088896340736f;
+  hipError_t e = mla::launch_decode_fp8(d, static_cast<const char*>(plan->dev), plan->off_segs, plan->off_wgs,
+                                        plan->off_lens, q_nope_absorbed, q_pe, kv_codes, kv_scales, num_pages,
+                                        block_table, bt_stride, seq_lens, scale_log2, out, lse, ws.o, ws.lse, ws.f,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "FP8 decode kernel launch");
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status mla_decode_fp8(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe, const void* kv_codes,
+                          const void* kv_scales, int64_t num_pages, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_lens, float softmax_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  mla_status s = mla_decode_fp8_partials(plan, q_nope_absorbed, q_pe, kv_codes, kv_scales, num_pages, block_table,
+                                         bt_stride, seq_lens, softmax_scale, out, lse, workspace, workspace_bytes,
+                                         stream);
+  if (s != MLA_OK) return s;
+  return mla_decode_combine(plan, out, lse, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe, const void* kv_cache,

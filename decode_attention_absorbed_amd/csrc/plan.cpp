@@ -125,13 +125,15 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
   p.page = page;
   p.num_cus = num_cus;
   p.rows = q_len * heads;
-  // One kernel shape: 4 waves (128 query rows) per workgroup, 32-key tiles,
-  // one workgroup per compute unit (its LDS ring takes 144 KB).
-  if (tuning.variant != 0 && tuning.variant != 1) {
+  // Two kernel shapes, both 4 waves (128 query rows) per workgroup and one
+  // workgroup per compute unit (LDS rings of 144 KB): the bf16 kernel's
+  // 32-key tiles (variant 1, the default) and the FP8 kernel's 64-key tiles
+  // (variant 2).
+  if (tuning.variant < 0 || tuning.variant > 2) {
     *err = "unknown kernel variant";
     return kInvalid;
   }
-  p.v = Variant{4, 32, 1};
+  p.v = tuning.variant == 2 ? Variant{4, 64, 1} : Variant{4, 32, 1};
   p.nrb = (p.rows + p.v.rows_per_block() - 1) / p.v.rows_per_block();
   p.lens.assign(lens, lens + batch);
   for (int32_t b = 0; b < batch; ++b) p.max_pages = std::max(p.max_pages, (lens[b] + page - 1) / page);
@@ -146,8 +148,9 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
   // Slots: each slot is executed by nrb workgroups (one per row block).
   int64_t max_slots = (int64_t)num_cus * p.v.wg_per_cu / p.nrb;
   if (max_slots < 1) max_slots = 1;
-  const double c0 = tuning.seg_overhead_tiles;
-  const double min_frag = tuning.min_fragment_tiles;
+  // the tunables count 32-key tiles
+  const double c0 = tuning.seg_overhead_tiles * 32.0 / T;
+  const double min_frag = tuning.min_fragment_tiles * 32.0 / T;
 
   // Smallest capacity (in whole tiles) whose greedy pass fits in max_slots.
   int64_t lo_c = std::max<int64_t>((int64_t)std::ceil(c0) + 1, (total_tiles + max_slots - 1) / max_slots);

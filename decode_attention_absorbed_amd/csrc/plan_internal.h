@@ -58,7 +58,8 @@ struct PlanData {
 struct PlanTuning {
   double seg_overhead_tiles = 8.0;  // cost of one extra piece, in 32-key tiles
   double min_fragment_tiles = 4.0;  // do not start a piece smaller than this when splitting
-  int32_t variant = 0;              // 0 = automatic; 1 = 4 waves x 32-key tiles (the only kernel)
+  int32_t variant = 0;              // 0 = automatic (1); 1 = 4 waves x 32-key tiles (bf16 kernel);
+                                    // 2 = 4 waves x 64-key tiles (FP8 kernel)
 };
 
 // Validate and build the host schedule.  Returns 0 on success, otherwise an

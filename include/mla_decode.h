@@ -163,6 +163,62 @@ mla_status mla_decode_partials(const mla_plan* plan,
 mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 latent cache.
+ *
+ * The Huawei report ("DeepSeek V3/R1 inference deployment best practices on
+ * Ascend servers", section 6.1) names 8-bit keys and values as the next step
+ * for MLA decode; these entry points take the cache in the OCP FP8 formats
+ * that gfx950's matrix cores read.  Same computation and output as
+ * mla_decode, except:
+ *
+ *  kv_codes   device uint8 [num_pages, page_size, 576]; 16-byte aligned.
+ *             E4M3 ("fn": bias 7, max 448, S.1111.111 = NaN) codes of the
+ *             row [c_kv (512) | k_pe (64)].
+ *  kv_scales  device uint8 [num_pages, page_size]; 4-byte aligned.  E8M0
+ *             scale of each token: row value = 2^(e - 127) * decode(code).
+ *             e must be <= 254 (255 is NaN in E8M0).
+ *  q_nope_absorbed, q_pe stay bf16; each block of 32 consecutive values of a
+ *             576-wide query row is quantized in the kernel to E4M3 codes
+ *             with its own E8M0 exponent (OCP MXFP8): f = the smallest
+ *             integer with max|q| * 2^-f <= 448, limited to [-127, 127],
+ *             codes = round-to-nearest-even of q * 2^-f (saturated at 448).
+ *
+ * The softmax weights are rounded to E4M3 for the PV product (the row's
+ * largest weight scaled into [64, 256]); the output therefore carries a
+ * relative error of a few percent of the weights' rounding, averaged over
+ * the keys; lse is unaffected.
+ *
+ * mla_decode_fp8_plan / _plan_host: as mla_decode_plan / _plan_host, for the
+ *   FP8 kernel (64-key tiles).  A plan of one kind is refused by the other
+ *   kind's decode calls (MLA_ERR_INVALID_ARGUMENT); mla_decode_combine,
+ *   mla_decode_workspace_bytes and the inspection calls take either.
+ * mla_decode_fp8 == mla_decode_fp8_partials + mla_decode_combine.
+ * Errors as for mla_decode.
+ */
+mla_status mla_decode_fp8_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                               int32_t num_heads, int32_t page_size, int32_t num_cus,
+                               mla_plan** plan_out);
+mla_status mla_decode_fp8_plan_host(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                                    int32_t num_heads, int32_t page_size, int32_t num_cus,
+                                    mla_plan** plan_out);
+mla_status mla_decode_fp8(const mla_plan* plan,
+                          const void* q_nope_absorbed, const void* q_pe,
+                          const void* kv_codes, const void* kv_scales, int64_t num_pages,
+                          const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_lens, float softmax_scale,
+                          float* out, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+mla_status mla_decode_fp8_partials(const mla_plan* plan,
+                                   const void* q_nope_absorbed, const void* q_pe,
+                                   const void* kv_codes, const void* kv_scales, int64_t num_pages,
+                                   const int32_t* block_table, int32_t bt_stride,
+                                   const int32_t* seq_lens, float softmax_scale,
+                                   float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Free a plan (its host memory and its device schedule).  NULL is a no-op.
  * The plan must not be in use by a kernel still running. */
 void mla_decode_plan_destroy(mla_plan* plan);

@@ -68,3 +68,48 @@ def test_no_store_data_hazards(asm):
     assert len(bodies) >= 4
     for body in bodies:
         assert asm_checks.store_data_hazards(body) == []
+
+
+# ---- the FP8 kernel ---------------------------------------------------------------------
+
+FP8_PREFIX = "_ZN3mla12_GLOBAL__N_117decode_fp8_kernel"
+
+
+@pytest.fixture(scope="module")
+def asm_fp8(tmp_path_factory):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc):
+        hipcc = shutil.which("hipcc")
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    from decode_attention_absorbed_amd.build import HIP_FLAGS
+
+    out = str(tmp_path_factory.mktemp("asm8") / "mla_decode_fp8.s")
+    flags = [f for f in HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "mla_decode_fp8.hip"), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read()
+
+
+def test_fp8_kernels_present(asm_fp8):
+    bodies = asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX)
+    assert len(bodies) == 3  # 1, 2 or 4 pages per 64-key tile
+    for b in bodies:
+        # 18 scaled QK^T MFMAs per tile (prologue tile + loop), 16 PV MFMAs
+        assert sum(t.startswith("v_mfma_scale_f32_32x32x64_f8f6f4") for t in b) >= 36
+        assert sum(t.startswith("v_mfma_f32_32x32x64_f8f6f4") for t in b) >= 32
+
+
+def test_fp8_hazards(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
+        assert asm_checks.mfma_hazards(body) == []
+        assert asm_checks.mfma_result_hazards(body) == []
+        assert asm_checks.store_data_hazards(body) == []
+
+
+def test_fp8_async_query_loads_untouched_until_waited(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
+        assert sum(t.startswith("global_load_dwordx4") for t in body) == 36
+        assert asm_checks.async_load_violations(body) == []

@@ -1,0 +1,183 @@
+"""FP8-cache decode (HIP, through the C ABI) against the fp64 FP8 oracle on an MI355X.
+
+Tolerance, derived from the arithmetic (the oracle module states the model):
+the scores use the same E4M3 query codes and exactly scaled keys on both sides,
+so lse differs only by fp32 rounding (bar: max-abs <= 1e-3, as for bf16).  The
+output differs mainly because the kernel rounds the softmax weights to E4M3
+before the PV product; ``fp8_weight_error_rms`` gives the root-mean-square
+size of that error per element.  Bars: the L2 norm of the error is at most
+2x the model's, and every element is within 8 model standard deviations
+(+ 1e-4 for fp32 rounding).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import decode_attention_absorbed_amd as mla  # noqa: E402
+from decode_attention_absorbed_amd import binding as bnd  # noqa: E402
+from oracle import dequantize_cache, fp8_weight_error_rms, mla_decode_fp8_ref  # noqa: E402
+from workloads import (  # noqa: E402
+    make_config_fp8,
+    make_inputs_fp8,
+    poison_tails_fp8,
+    poison_unreferenced_fp8,
+)
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX_ABS = 1e-3
+RMS_FACTOR, SIGMAS, ABS_FLOOR = 2.0, 8.0, 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run_gpu(x, dev, num_cus=0, seq_lens_dev=None, block_table=None, plan=None):
+    t = x.to_torch(dev)
+    if plan is None:
+        plan = bnd.mla_decode_fp8_plan(x.seq_lens, x.q_len, x.heads, x.page, num_cus)
+    bt = t["block_table"] if block_table is None else block_table
+    sl = t["seq_lens"] if seq_lens_dev is None else seq_lens_dev
+    out, lse = bnd.mla_decode_fp8(plan, t["q_nope"], t["q_pe"], t["cache_codes"], t["cache_exps"], bt, sl, x.softmax_scale)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def oracle(x, idx=None):
+    idx = np.arange(x.batch) if idx is None else np.asarray(idx)
+    args = (x.q_nope_f64()[idx], x.q_pe_f64()[idx], x.cache_codes, x.cache_exps, x.block_table[idx], x.seq_lens[idx], x.softmax_scale)
+    o, l = mla_decode_fp8_ref(*args)
+    rms = fp8_weight_error_rms(*args)
+    return o, l, rms
+
+
+def compare(out, lse, ref_o, ref_l, rms, what=""):
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)), f"{what}: non-finite output"
+    err = out - ref_o
+    e_l = float(np.max(np.abs(lse - ref_l)))
+    ratio = float(np.linalg.norm(err) / max(np.linalg.norm(rms), 1e-300))
+    worst = float(np.max(np.abs(err) / (SIGMAS * rms + ABS_FLOOR)))
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref_o), 1e-300))
+    print(
+        f"{what}: out max-abs {np.max(np.abs(err)):.3e} rel-L2 {rel:.3e} | L2 / model {ratio:.3f} "
+        f"| worst element / bar {worst:.3f} | lse max-abs {e_l:.3e}",
+        flush=True,
+    )
+    assert e_l <= LSE_MAX_ABS, f"{what}: lse max-abs {e_l}"
+    assert ratio <= RMS_FACTOR, f"{what}: error L2 is {ratio:.2f}x the model's"
+    assert worst <= 1.0, f"{what}: an element is {worst:.2f}x past its bar"
+
+
+SMALL = [
+    # (batch, heads, q_len, page, lens)
+    (2, 16, 1, 16, [37, 100]),
+    (3, 128, 1, 64, [1, 64, 200]),
+    (3, 128, 2, 64, [2, 65, 300]),
+    (4, 64, 1, 32, [31, 32, 33, 257]),
+    (2, 100, 1, 16, [129, 17]),
+    (2, 64, 3, 128, [3, 400]),
+    (5, 128, 1, 256, [1000, 1, 513, 64, 300]),
+    (1, 32, 8, 16, [111]),
+    (3, 128, 4, 16, [1000, 257, 31]),
+    (2, 128, 8, 32, [700, 9]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}" for c in SMALL])
+def test_fp8_small_cases(dev, case):
+    B, H, q, P, lens = case
+    x = make_inputs_fp8(B, H, q, P, lens, seed=200 + sum(lens))
+    out, lse = run_gpu(x, dev)
+    compare(out, lse, *oracle(x), what=str(case))
+
+
+@pytest.mark.parametrize("num_cus", [1, 7, 256])
+def test_fp8_forced_split_counts(dev, num_cus):
+    x = make_inputs_fp8(3, 128, 2, 64, [1500, 700, 90], seed=25)
+    out, lse = run_gpu(x, dev, num_cus=num_cus)
+    compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
+
+
+SAMPLES = {"tiny": None, "dsv3": [0, 31], "mtp": "extremes", "mixed": "mixed", "long": None}
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp", "mixed", "long"])
+def test_fp8_named_workload_parity(dev, name):
+    x = make_config_fp8(name)
+    print(f"{name}: B={x.batch} H={x.heads} q_len={x.q_len} pages={x.num_pages}", flush=True)
+    out, lse = run_gpu(x, dev)
+    s = SAMPLES[name]
+    if s == "extremes":
+        idx = [int(np.argmin(x.seq_lens)), int(np.argmax(x.seq_lens))]
+    elif s == "mixed":
+        idx = list(np.flatnonzero(x.seq_lens == 20480)[:1]) + list(np.flatnonzero(x.seq_lens == 400)[:2])
+    else:
+        idx = list(range(x.batch)) if s is None else s
+    compare(out[idx], lse[idx], *oracle(x, idx), what=f"{name} requests {idx}")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_fp8_page_permutation_is_bitwise_invariant(dev):
+    x = make_inputs_fp8(3, 128, 1, 16, [300, 47, 129], seed=29)
+    o1, l1 = run_gpu(x, dev)
+    perm = np.random.default_rng(1).permutation(x.num_pages)
+    codes2 = np.empty_like(x.cache_codes)
+    exps2 = np.empty_like(x.cache_exps)
+    codes2[perm] = x.cache_codes
+    exps2[perm] = x.cache_exps
+    x.block_table = np.where(x.block_table >= 0, perm[np.maximum(x.block_table, 0)], -1).astype(np.int32)
+    x.cache_codes, x.cache_exps = codes2, exps2
+    o2, l2 = run_gpu(x, dev)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_fp8_nan_tails_and_unreferenced_pages_never_reach_the_output(dev):
+    x = make_inputs_fp8(3, 128, 2, 64, [100, 65, 7], seed=31, extra_pages=3)
+    o1, l1 = run_gpu(x, dev)
+    poison_tails_fp8(x)
+    poison_unreferenced_fp8(x)
+    o2, l2 = run_gpu(x, dev)
+    assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_fp8_single_visible_key_returns_its_latent_row(dev):
+    x = make_inputs_fp8(2, 128, 1, 16, [1, 1], seed=34)
+    out, lse = run_gpu(x, dev)
+    ref_o, ref_l, _ = oracle(x)
+    cache = dequantize_cache(x.cache_codes, x.cache_exps)
+    for b in range(2):
+        row = cache[x.block_table[b, 0], 0, :512]
+        # one key, weight 1: P' rounds to 2^6 exactly, so out is the
+        # dequantized row up to fp32 rounding of the weight (1 - p ~ 1e-7)
+        np.testing.assert_allclose(out[b, 0], np.broadcast_to(row, (128, 512)), rtol=2e-6, atol=1e-6)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-4)
+
+
+def test_fp8_repeat_runs_are_bitwise_identical(dev):
+    x = make_inputs_fp8(4, 128, 1, 64, [2000, 5, 640, 999], seed=33)
+    a = run_gpu(x, dev)
+    b = run_gpu(x, dev)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_fp8_plan_and_kernel_kinds_do_not_mix(dev):
+    x = make_inputs_fp8(1, 16, 1, 16, [40], seed=35)
+    t = x.to_torch(dev)
+    p16 = mla.mla_decode_plan(x.seq_lens, 1, 16, 16)
+    with pytest.raises(bnd.MLAError):
+        bnd.mla_decode_fp8(p16, t["q_nope"], t["q_pe"], t["cache_codes"], t["cache_exps"], t["block_table"], t["seq_lens"], 0.1)
+    p8 = bnd.mla_decode_fp8_plan(x.seq_lens, 1, 16, 16)
+    cache_bf16 = torch.zeros((x.num_pages, 16, 576), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(bnd.MLAError):
+        mla.mla_decode(p8, t["q_nope"], t["q_pe"], cache_bf16, t["block_table"], t["seq_lens"], 0.1)

@@ -359,3 +359,25 @@ def make_config_fp8(name: str, seed: Optional[int] = None) -> MLAInputsFP8:
         seed=c["seed"] if seed is None else seed,
         name=name,
     )
+
+
+def poison_tails_fp8(x: MLAInputsFP8) -> None:
+    """NaN codes (0x7F) and NaN scale bytes (255) in the unused slots of every
+    request's last page (in place)."""
+    for b in range(x.batch):
+        L = int(x.seq_lens[b])
+        n = -(-L // x.page)
+        tail = L - (n - 1) * x.page
+        if tail < x.page:
+            x.cache_codes[x.block_table[b, n - 1], tail:, :] = 0x7F
+            x.cache_exps[x.block_table[b, n - 1], tail:] = 255
+
+
+def poison_unreferenced_fp8(x: MLAInputsFP8) -> None:
+    """NaN codes and scale bytes in every page no request references (in place)."""
+    ref = np.zeros(x.num_pages, dtype=bool)
+    for b in range(x.batch):
+        n = -(-int(x.seq_lens[b]) // x.page)
+        ref[x.block_table[b, :n]] = True
+    x.cache_codes[~ref] = 0x7F
+    x.cache_exps[~ref] = 255
