@@ -11,7 +11,11 @@ larger than 1 GB).
 
 Prints ONE JSON line (value = algorithmic TFLOP/s of the whole step).
 
-    python bench.py [--config dsv3] [--steps 50] [--warmup 10]
+    python bench.py [--config dsv3] [--steps 50] [--warmup 10] [--kv bf16|fp8]
+
+With --kv fp8 the same workload runs over an FP8 cache (E4M3 codes with
+per-token E8M0 scales; seeded codes of the same N(0, 1) draw) on the FP8
+kernel, against the FP8 matrix peak.
 
 HBM traffic evidence (roofline.traffic): rocprofv3 counter passes over this
 script, one counter per pass, for the decode workload and for a plain device
@@ -41,6 +45,10 @@ def kernel_sha() -> str:
         if p.endswith((".hip", ".cpp", ".h", ".inc")):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
+
+
+def traffic_name(config: str, kv: str) -> str:
+    return config if kv == "bf16" else f"{config}_{kv}"
 
 
 def load_traffic(config: str, per_launch_bytes_alg: int):
@@ -101,8 +109,9 @@ def traffic_from(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     cf_k, cw_k = max(cf), max(cw)
     f_fetch = COPY_BYTES / (cf_k * 1024.0)
     f_write = COPY_BYTES / (cw_k * 1024.0)
-    fetch = med(_counter_per_dispatch(fetch_dir, "FETCH_SIZE", "decode_kernel"))
-    write = med(_counter_per_dispatch(write_dir, "WRITE_SIZE", "decode_kernel"))
+    kname = "decode_fp8_kernel" if config.endswith("_fp8") else "decode_kernel<"
+    fetch = med(_counter_per_dispatch(fetch_dir, "FETCH_SIZE", kname))
+    write = med(_counter_per_dispatch(write_dir, "WRITE_SIZE", kname))
     cfetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "combine_kernel")
     cwrite = _counter_per_dispatch(write_dir, "WRITE_SIZE", "combine_kernel")
     res = {
@@ -160,29 +169,32 @@ def cpu_baseline(x, seconds: float) -> dict:
     }
 
 
-def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float) -> dict:
+def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float, kv: str = "bf16") -> dict:
     import torch
 
     import decode_attention_absorbed_amd as mla
     from decode_attention_absorbed_amd import accounting as acc
     from decode_attention_absorbed_amd import binding as bnd
-    from workloads import CONFIGS, make_config
+    from workloads import make_config, make_config_fp8
 
     dev = torch.device("cuda:0")
-    x = make_config(config)
+    fp8 = kv == "fp8"
+    x = make_config_fp8(config) if fp8 else make_config(config)
     lens = [int(v) for v in x.seq_lens]
-    roof = acc.roofline_seconds(lens, x.heads, x.q_len, x.page)
+    roof = acc.roofline_seconds(lens, x.heads, x.q_len, x.page, kv)
 
     t = x.to_torch(dev)
-    kv_bytes = t["cache"].numel() * 2
+    cache_t = t["cache_codes"] if fp8 else t["cache"]
+    kv_bytes = cache_t.numel() * cache_t.element_size()
     copies = max(1, min(16, -(-(1 << 30) // max(kv_bytes, 1))))
-    caches = [t["cache"]] + [t["cache"].clone() for _ in range(copies - 1)]
+    caches = [cache_t] + [cache_t.clone() for _ in range(copies - 1)]
+    scales = ([t["cache_exps"]] + [t["cache_exps"].clone() for _ in range(copies - 1)]) if fp8 else None
     qns = [t["q_nope"]] + [t["q_nope"].clone() for _ in range(copies - 1)]
     qps = [t["q_pe"]] + [t["q_pe"].clone() for _ in range(copies - 1)]
     bt, sl = t["block_table"], t["seq_lens"]
 
     tp0 = time.perf_counter()
-    plan = mla.mla_decode_plan(x.seq_lens, x.q_len, x.heads, x.page)
+    plan = (bnd.mla_decode_fp8_plan if fp8 else mla.mla_decode_plan)(x.seq_lens, x.q_len, x.heads, x.page)
     plan_ms = (time.perf_counter() - tp0) * 1e3
     B, H, q = x.batch, x.heads, x.q_len
     out = torch.empty((B, q, H, 512), dtype=torch.float32, device=dev)
@@ -193,13 +205,14 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
 
     def partials(i):
         c = i % copies
-        bnd._check(
-            L.mla_decode_partials(
-                plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(), int(caches[c].shape[0]),
-                bt.data_ptr(), int(bt.shape[1]), sl.data_ptr(), float(x.softmax_scale), out.data_ptr(),
-                lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream,
-            )
-        )
+        tail = (bt.data_ptr(), int(bt.shape[1]), sl.data_ptr(), float(x.softmax_scale), out.data_ptr(),
+                lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream)
+        if fp8:
+            bnd._check(L.mla_decode_fp8_partials(plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(),
+                                                 scales[c].data_ptr(), int(caches[c].shape[0]), *tail))
+        else:
+            bnd._check(L.mla_decode_partials(plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(),
+                                             int(caches[c].shape[0]), *tail))
 
     def combine():
         bnd._check(L.mla_decode_combine(plan.handle, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream))
@@ -257,8 +270,8 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
         peak, unit = acc.PEAK_HBM_BYTES_PER_S / 1e9, "GB/s"
     else:
         achieved = flops / (dec_burst * 1e-3) / 1e12
-        peak, unit = acc.PEAK_BF16_FLOPS / 1e12, "TFLOP/s"
-    traffic = load_traffic(config, nbytes)
+        peak, unit = (acc.PEAK_FP8_FLOPS if fp8 else acc.PEAK_BF16_FLOPS) / 1e12, "TFLOP/s"
+    traffic = load_traffic(traffic_name(config, kv), nbytes)
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -270,10 +283,12 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, random page permutation)",
+        "dtype": "fp8" if fp8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) bf16 queries, E4M3 cache codes of N(0,1) draws with per-token E8M0 "
+                 "scales, random page permutation)") if fp8 else "synthetic (seeded N(0,1) bf16, random page permutation)",
         "config": {
-            "workload": config,
+            "workload": config if not fp8 else f"{config}-fp8",
+            "kv_dtype": kv,
             "batch": B,
             "heads": H,
             "q_len": q,
@@ -289,7 +304,7 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
             "unit": unit,
             "frac": achieved / peak,
             "traffic": traffic,
-            "kernel": "decode_kernel",
+            "kernel": "decode_fp8_kernel" if fp8 else "decode_kernel",
             "duration_ms": dec_burst,
         },
         "step_roofline_frac": roof["t_bound"] / (ms_step * 1e-3),
@@ -320,6 +335,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long")
     ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true", help="run the plain copy the traffic counters are scaled by")
@@ -327,7 +343,7 @@ def main() -> int:
                     help="write profiles/traffic_<config>.json from rocprofv3 counter output (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_from:
-        return traffic_from(args.config, *args.traffic_from)
+        return traffic_from(traffic_name(args.config, args.kv), *args.traffic_from)
     if args.calibrate_copy:
         return calibrate_copy()
     if args.gpus != 1:
@@ -336,9 +352,10 @@ def main() -> int:
         return 2
     if args.all:
         for name in ["tiny", "dsv3", "mtp", "mixed", "long"]:
-            r = run(name, args.steps, args.warmup, False, 0.0)
+            r = run(name, args.steps, args.warmup, False, 0.0, args.kv)
             print(json.dumps(r), file=sys.stderr, flush=True)
-    res = run(args.config, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+    res = run(args.config, args.steps, args.warmup, not args.no_cpu_baseline and args.kv == "bf16", args.cpu_seconds,
+              args.kv)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -7,9 +7,10 @@ query against all L keys; by default this module counts only the keys a query
 may see (query j of a request with L keys sees L - q_len + 1 + j).
 
 Bytes are the compulsory HBM traffic: the cached rows of every request
-(576 bf16 each), the queries, the fp32 outputs and lse, the block table
-entries read and the sequence lengths.  Partials and re-reads are not counted,
-so they show up as a lower roofline fraction.
+(576 bf16 each, or 576 E4M3 codes plus one scale byte for the FP8 cache), the
+queries, the fp32 outputs and lse, the block table entries read and the
+sequence lengths.  Partials and re-reads are not counted, so they show up as
+a lower roofline fraction.
 """
 from __future__ import annotations
 
@@ -17,10 +18,12 @@ from typing import Sequence
 
 D_QK, D_V = 576, 512
 ROW_BYTES = D_QK * 2  # bf16 row per cached token
+ROW_BYTES_FP8 = D_QK + 1  # E4M3 codes + the E8M0 scale byte
 
-# MI355X published peaks (dense): HBM3E 8 TB/s, bf16 MFMA 2.5 PFLOP/s.
+# MI355X published peaks (dense): HBM3E 8 TB/s, bf16 MFMA 2.5 PFLOP/s, fp8 MFMA 5.0 PFLOP/s.
 PEAK_HBM_BYTES_PER_S = 8.0e12
 PEAK_BF16_FLOPS = 2.5e15
+PEAK_FP8_FLOPS = 5.0e15
 
 
 def visible_key_count(seq_lens: Sequence[int], q_len: int) -> int:
@@ -32,25 +35,25 @@ def flops(seq_lens: Sequence[int], heads: int, q_len: int, visible: bool = True)
     return 2 * (D_QK + D_V) * heads * keys
 
 
-def kv_bytes(seq_lens: Sequence[int]) -> int:
-    return ROW_BYTES * sum(int(L) for L in seq_lens)
+def kv_bytes(seq_lens: Sequence[int], kv: str = "bf16") -> int:
+    return (ROW_BYTES_FP8 if kv == "fp8" else ROW_BYTES) * sum(int(L) for L in seq_lens)
 
 
-def algorithmic_bytes(seq_lens: Sequence[int], heads: int, q_len: int, page: int) -> int:
+def algorithmic_bytes(seq_lens: Sequence[int], heads: int, q_len: int, page: int, kv: str = "bf16") -> int:
     B = len(seq_lens)
     rows = B * q_len * heads
     q = rows * D_QK * 2
     out = rows * D_V * 4 + rows * 4
     bt = 4 * sum(-(-int(L) // page) for L in seq_lens) + 4 * B
-    return kv_bytes(seq_lens) + q + out + bt
+    return kv_bytes(seq_lens, kv) + q + out + bt
 
 
-def roofline_seconds(seq_lens: Sequence[int], heads: int, q_len: int, page: int) -> dict:
-    """Time at the HBM and MFMA peaks and which one binds."""
+def roofline_seconds(seq_lens: Sequence[int], heads: int, q_len: int, page: int, kv: str = "bf16") -> dict:
+    """Time at the HBM and MFMA peaks (bf16 or fp8 matrix rate) and which one binds."""
     f = flops(seq_lens, heads, q_len)
-    b = algorithmic_bytes(seq_lens, heads, q_len, page)
+    b = algorithmic_bytes(seq_lens, heads, q_len, page, kv)
     t_hbm = b / PEAK_HBM_BYTES_PER_S
-    t_mfma = f / PEAK_BF16_FLOPS
+    t_mfma = f / (PEAK_FP8_FLOPS if kv == "fp8" else PEAK_BF16_FLOPS)
     return {
         "flops": f,
         "bytes": b,

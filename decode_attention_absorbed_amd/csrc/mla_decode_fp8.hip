@@ -14,13 +14,14 @@
 //  * QK^T runs on v_mfma_scale_f32_32x32x64_f8f6f4: the key scale (per token)
 //    and the query block scale ride along as the instruction's per-lane scale
 //    operands, so the fp32 scores come out fully scaled at no extra cost;
-//  * PV runs on v_mfma_f32_32x32x64_f8f6f4 with P rounded to E4M3.  V's
-//    per-token scale goes into P: p_t * 2^(e_t - E_ref + 6), with E_ref the
-//    largest scale byte seen so far by the wave (a lazy reference like the
-//    softmax maximum: the output is rescaled when it grows).  With the row's
-//    softmax reference allowed to trail its maximum by at most 2 (log2 units),
-//    every scaled weight is <= 2^8 < 448 and a row's largest weight lands in
-//    [2^6, 2^8], where E4M3 keeps 3 mantissa bits.
+//  * PV runs on the same scaled instruction with P rounded to E4M3.  V's
+//    per-token scale goes into P: p_t 2^(e_t - E + 6), E the largest scale
+//    byte of the tile, and each tile's weights are taken relative to
+//    2^x (x = floor of the tile's row maximum above the row's reference), so
+//    the tile's largest weight lands in [2^6, 2^7), where E4M3 keeps 3
+//    mantissa bits; 2^x and the tile's E go back in exactly through the P^T
+//    scale operand.  The output therefore needs no rescale when a row's
+//    maximum grows (only a growth beyond 2^32 moves the reference).
 //
 // Structure (one workgroup = 4 waves = 128 query rows; rows are the flattened
 // (query token, head) pairs of one request):
@@ -67,7 +68,7 @@ constexpr int kCopiesPerWave8 = kLoadsPerWave8 + 1;            // + the scale by
 constexpr int kScaleArea8 = 256;                          // one wave's copy of a tile's scale bytes
 constexpr int kKSteps8 = 576 / 64;                        // 9 K steps of QK^T
 constexpr int kWeightExp8 = 6;                            // P is scaled by 2^6 before rounding
-constexpr float kThreshold8 = 2.0f;                       // lazy reference step, log2 units
+constexpr float kRefStep8 = 32.0f;                        // reference moves past this (log2 units)
 constexpr float kLn2_8 = 0.69314718055994530942f;
 constexpr float kMuFloor8 = -1e30f;
 constexpr int kLdsBytes8 = kStages8 * kStageBytes8 + kStages8 * kWaves8 * kScaleArea8 + kWaves8 * 256;
@@ -237,8 +238,12 @@ struct QBlock {
   int e8m0;
 };
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Packed unsigned 16-bit max of two words (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 __device__ __forceinline__ int block_exponent(float amax) {
   // amax = m 2^x with m in [0.5, 1); 448 = 0.875 * 2^9: f = x - 9 if
@@ -251,6 +256,7 @@ __device__ __forceinline__ int block_exponent(float amax) {
 
 __device__ __forceinline__ QBlock quantize_block(const bf16x8 (&v)[4], int g) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef short i16x2 __attribute__((ext_vector_type(2)));
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -258,30 +264,29 @@ __device__ __forceinline__ QBlock quantize_block(const bf16x8 (&v)[4], int g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[4 * i + j] = u[j];
   }
-  // largest magnitude of each half (exact: a max of bf16 values), then of
-  // each block with the partner lane's half
-  float am[2] = {0.f, 0.f};
+  // Largest magnitude of each half: the bf16 bit patterns without their sign
+  // order like the magnitudes, so a packed 16-bit max finds it exactly.
+  float am[2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float a;
-    asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(a) : "v"(am[i >> 3]), "v"(bf16_lo(w[i])), "v"(bf16_hi(w[i])));
-    am[i >> 3] = a;
+  for (int h = 0; h < 2; ++h) {
+    uint32_t m = w[8 * h] & 0x7fff7fffu;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = pk_max_u16(m, w[8 * h + i] & 0x7fff7fffu);
+    am[h] = __uint_as_float(max(m & 0xffffu, m >> 16) << 16);
   }
   int f[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) f[h] = block_exponent(pair_max(am[h]));
+  // v_cvt_scalef32_pk_fp8_bf16 rounds (x / scale) to E4M3, nearest even:
+  // scale = 2^f is exact.
   QBlock q;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float sc = __builtin_ldexpf(1.f, -f[i >> 2]);  // exact power of two
-    // |x| * 2^-f <= 448 by construction; the clamp only guards the limits
-    const float a0 = fminf(fmaxf(bf16_lo(w[2 * i]) * sc, -448.f), 448.f);
-    const float a1 = fminf(fmaxf(bf16_hi(w[2 * i]) * sc, -448.f), 448.f);
-    const float a2 = fminf(fmaxf(bf16_lo(w[2 * i + 1]) * sc, -448.f), 448.f);
-    const float a3 = fminf(fmaxf(bf16_hi(w[2 * i + 1]) * sc, -448.f), 448.f);
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, c, true);
-    q.codes[i] = c;
+    const float sc = __builtin_ldexpf(1.f, f[i >> 2]);
+    i16x2 c = {0, 0};
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(c, __builtin_bit_cast(bf16x2, w[2 * i]), sc, false);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(c, __builtin_bit_cast(bf16x2, w[2 * i + 1]), sc, true);
+    q.codes[i] = __builtin_bit_cast(int, c);
   }
   q.e8m0 = 127 + (g ? f[1] : f[0]);
   return q;
@@ -487,36 +492,42 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     TilePages8<NPG> pg_raw = fetch_pages(kv0 + min(3, last_tile) * kTile8);
 
     // ---- per-tile scale handling (this wave's copy of the tile's bytes) ----
-    // ea[kb]: scale byte of key 32kb + l32 (the QK^T A-operand scale);
-    // E_ref: the wave's reference exponent; sc (LDS, per wave): the factor
-    // 2^(e_t - E_ref + 6) of every key of the tile, read back per lane.
-    int e_ref = -1;          // no tile seen yet
-    bool e_moved = false;    // E_ref grew on the tile just prepared
-    float e_alpha = 1.f;     // 2^(E_ref_old - E_ref_new) for the output
+    // ea[kb]: scale byte of key 32kb + l32 (the QK^T A-operand scale).
+    // E_tile: the largest scale byte of the tile's keys; sc (LDS, per wave):
+    // 2^(e_t - E_tile + 6) for every key t of the tile, read back per lane.
+    // e0: E_tile of the piece's first tile; a tile's P carries
+    // 2^(E_tile - e0) in its PV scale operand, so the output accumulates
+    // p_t 2^(e_t - e0 + 6) codes_t throughout.  Only a tile more than 2^64
+    // above e0 moves e0 (and rescales the output).
+    int e0 = -1;
+    int de = 0;              // E_tile - e0 of the tile just prepared
+    bool e_moved = false;    // e0 moved on it
+    float e_alpha = 1.f;     // 2^(e0_old - e0_new)
     int ea[2];
     const uint32_t sc_base = lds_addr(sc_lds + wave * 256);
     // Keys past the piece (tb + k >= kv1) take the neutral byte 127 for QK^T
-    // and 0 for the reference: the copied 4-byte groups may hold bytes of
-    // slots past the request's end, which must not steer anything.
+    // and 0 for E_tile: the copied 4-byte groups may hold bytes of slots past
+    // the request's end, which must not steer anything.
     auto prep_scales = [&](int stage, int tb_s) {
       const uint8_t* sa = scl_lds + (stage * kWaves8 + wave) * kScaleArea8;
-      const int e0 = *LDS_AS(const uint8_t, (uintptr_t)lds_addr(sa + l32));
-      const int e1 = *LDS_AS(const uint8_t, (uintptr_t)lds_addr(sa + 32 + l32));
+      const int e0b = *LDS_AS(const uint8_t, (uintptr_t)lds_addr(sa + l32));
+      const int e1b = *LDS_AS(const uint8_t, (uintptr_t)lds_addr(sa + 32 + l32));
       const bool v0 = tb_s + l32 < kv1, v1 = tb_s + 32 + l32 < kv1;
-      ea[0] = v0 ? e0 : 127;
-      ea[1] = v1 ? e1 : 127;
-      const int ej = g ? (v1 ? e1 : 0) : (v0 ? e0 : 0);  // key `lane` of the tile
+      ea[0] = v0 ? e0b : 127;
+      ea[1] = v1 ? e1b : 127;
+      const int ej = g ? (v1 ? e1b : 0) : (v0 ? e0b : 0);  // key `lane` of the tile
       const int et = __builtin_amdgcn_readfirstlane(wave_max_u32(ej));
       e_moved = false;
       e_alpha = 1.f;
-      if (et > e_ref) {
-        if (e_ref >= 0) {
-          e_moved = true;
-          e_alpha = __builtin_ldexpf(1.f, e_ref - et);
-        }
-        e_ref = et;
+      if (e0 < 0) {
+        e0 = et;
+      } else if (et - e0 > 64) {
+        e_moved = true;
+        e_alpha = __builtin_ldexpf(1.f, e0 - et);
+        e0 = et;
       }
-      const int ex = ej - e_ref + 127 + kWeightExp8;
+      de = et - e0;
+      const int ex = ej - et + 127 + kWeightExp8;
       const float sc = ex > 0 ? __int_as_float(ex << 23) : 0.f;
       *LDS_AS(float, (uintptr_t)(sc_base + 4 * lane)) = sc;
     };
@@ -556,30 +567,39 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
           i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)((base ^ 256u) + 18432))));
       dst = i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
     };
-    auto pv_tile = [&](int stage, const i32x8& pt, auto&& extra) {
+    const int one_e8m0 = 127;  // V^T is not scaled
+    auto pv_tile = [&](int stage, const i32x8& pt, int pscale, auto&& extra) {
       i32x8 v[2];
       read_v(stage, 0, v[0]);
       static_for<16>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
         if constexpr (cb + 1 < 16) read_v(stage, cb + 1, v[(cb + 1) & 1]);
         extra(cb);
-        OBlock8<cb>::mfma(v[cb & 1], pt);
+        OBlock8<cb>::mfma(v[cb & 1], pt, one_e8m0, pscale);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
 
-    // ---- online softmax state (base 2, lazy reference, one row per lane) ----
-    float m_ref = -INFINITY, mu = kMuFloor8, l_part = 0.f, alpha_o = 1.f;
+    // ---- online softmax state (base 2, one row per lane) ----
+    // mu: the row's reference (log2 units), set by its first finite maximum
+    // and moved only when the maximum passes it by more than kRefStep8 (an
+    // fp32 range guard; the output is then rescaled).  Each tile's weights
+    // are taken relative to mu + x, x = floor(tile max - mu), so that the
+    // tile's largest weight times 2^6 lands in [2^6, 2^7) before rounding to
+    // E4M3; 2^x goes back in through the PV scale operand (with 2^de).
+    float mu = kMuFloor8, l_part = 0.f, alpha_o = 1.f;
     bool any_scale = false;
-    float mx = 0.f;
+    float mx = 0.f, mu_t = 0.f, px = 1.f;
+    int psc = 127;  // PV scale byte of the tile in flight
     // Softmax of one tile of scores s (s[kb][4a + b] = key tb_s + 32kb + 8a +
     // 4g + b of this lane's row), in kSmSteps8 steps spread between MFMAs:
     //   0-1: mask block kb's keys past the row's limit (tiles that need it),
-    //   2: the lane's max, 3: the row max (lane pair) and reference update,
-    //   4-11: a = step - 4 (kb = a / 4): p = 2^(s*scale - mu), running sum,
-    //         P' = p * sc, and the E4M3 word of P^T (K slots 4(4kb + a%4)..).
+    //   2: the lane's max, 3: the row max (lane pair), reference and x,
+    //   4-11: a = step - 4 (kb = a / 4): p = 2^(s*scale - mu - x), running
+    //         sum p 2^x, P' = p * sc, and the E4M3 word of P^T (K slots
+    //         4(4kb + a%4)..).
     constexpr int kSmSteps8 = 12;
-    auto softmax_step = [&](int step, f32x16(&s)[2], bool need_mask, int tb_s, i32x8& pt) {
+    auto softmax_step = [&](int step, f32x16(&s)[2], bool need_mask, int tb_s, i32x8& pt, int& pscale) {
       if (step < 2) {
         const int kb = step;
         if (__builtin_amdgcn_readfirstlane((int)need_mask)) {
@@ -597,28 +617,33 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         mx = max3(m0, m1, max3(m2, m3, m3));
       } else if (step == 3) {
         mx = pair_max(mx);
-        // The reference moves only when the row maximum passes it by more
-        // than kThreshold8; mu = max(m_ref, floor) is what is subtracted, so
-        // the factor needs no case for -inf (0 on a row's first finite max).
         const float m = mx * scale_log2;
-        const bool upd = m > m_ref + kThreshold8;
-        const float m_new = upd ? m : m_ref;
-        const float mu_new = fmaxf(m_new, kMuFloor8);
-        const float alpha = __builtin_amdgcn_exp2f(mu - mu_new);
-        l_part *= alpha;
+        const bool fin = m > kMuFloor8;
         const bool had = mu > kMuFloor8;
+        float alpha = 1.f;
+        if (fin && !had) {
+          mu = m;  // first finite maximum: nothing accumulated yet
+        } else if (fin && m > mu + kRefStep8) {
+          alpha = __builtin_amdgcn_exp2f(mu - m);
+          mu = m;
+        }
+        l_part *= alpha;
         alpha_o = alpha * e_alpha;
-        any_scale = any_scale || (had && (upd || e_moved));
-        m_ref = m_new;
-        mu = mu_new;
+        any_scale = any_scale || (had && (alpha != 1.f || e_moved));
+        // x = floor(m - mu), with x + de kept inside the E8M0 range
+        int x = fin ? (int)__builtin_floorf(m - mu) : 0;
+        x = min(max(x + de, -127), 127) - de;
+        mu_t = mu + (float)x;
+        px = __builtin_ldexpf(1.f, x);
+        pscale = 127 + x + de;
       } else if (step < kSmSteps8) {
         const int q = step - 4, kb = q >> 2, a = q & 3;
         const f32x4 sc = *LDS_AS(const f32x4, (uintptr_t)(sc_base + 4 * (32 * kb + 8 * a + 4 * g)));
         float p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * a + j], scale_log2, -mu));
-          l_part += p[j];
+          p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * a + j], scale_log2, -mu_t));
+          l_part = __builtin_fmaf(p[j], px, l_part);
         }
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * sc[0], p[1] * sc[1], 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * sc[2], p[3] * sc[3], w, true);
@@ -636,7 +661,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       qk_tile(0, s0, [](int) {});
       const bool nm0 = kv0 + kTile8 > lim_wave;
 #pragma unroll
-      for (int step = 0; step < kSmSteps8; ++step) softmax_step(step, s0, nm0, kv0, pt);
+      for (int step = 0; step < kSmSteps8; ++step) softmax_step(step, s0, nm0, kv0, pt, psc);
       any_scale = false;  // nothing accumulated yet
     }
 
@@ -662,6 +687,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       };
       f32x16 s_next[2];
       i32x8 pt_next = pt;
+      int psc_next = psc;
       if (has_next) {
         prep_scales(st_next, tb + kTile8);
         qk_tile(st_next, s_next, [&](int k) {
@@ -675,8 +701,8 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
 
       if (has_next) {
         const bool nm = tb + 2 * kTile8 > lim_wave;
-        pv_tile(st_cur, pt, [&](int cb) {
-          if (cb >= 2 && cb - 2 < kSmSteps8) softmax_step(cb - 2, s_next, nm, tb + kTile8, pt_next);
+        pv_tile(st_cur, pt, psc, [&](int cb) {
+          if (cb >= 2 && cb - 2 < kSmSteps8) softmax_step(cb - 2, s_next, nm, tb + kTile8, pt_next, psc_next);
         });
         if (__any(any_scale)) {
           o8_drain();
@@ -684,8 +710,9 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         }
         any_scale = false;
         pt = pt_next;
+        psc = psc_next;
       } else {
-        pv_tile(st_cur, pt, [](int) {});
+        pv_tile(st_cur, pt, psc, [](int) {});
       }
       pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile8);
     }
@@ -695,10 +722,10 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     // ---- epilogue ----
     o8_drain();
     const float l_tot = pair_sum(l_part);
-    float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2_8 : -INFINITY;
+    float lse_v = l_tot > 0.f ? (mu + __builtin_amdgcn_logf(l_tot)) * kLn2_8 : -INFINITY;
     if (bad_len) lse_v = NAN;
-    // O holds sum_t p_t 2^(e_t - E_ref + 6) codes_t = 2^(133 - E_ref) sum_t p_t V_t.
-    const int oexp = e_ref - 127 - kWeightExp8;
+    // O holds sum_t p_t 2^(e_t - e0 + 6) codes_t = 2^(133 - e0) sum_t p_t V_t.
+    const int oexp = e0 - 127 - kWeightExp8;
     if (sg.partial < 0) {
       float inv = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, oexp) : 0.f;
       if (bad_len) inv = NAN;
