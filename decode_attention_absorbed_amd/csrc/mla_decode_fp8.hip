@@ -189,19 +189,28 @@ __device__ __forceinline__ float o8_absmax_rec(float m) {
   return m;
 }
 
-// Final fp32 output of the lane's row: block cb, register quad i goes to
-// columns 32cb + 8i + 4(l/32) .. +3 (dst already holds the 4(l/32)).
-template <int CB>
-__device__ __forceinline__ void o8_store_rec(float* dst, float inv) {
-  if constexpr (CB < 16) {
-    constexpr int r = 16 * CB;
-    store_wt(dst + 32 * CB + 0, f32x4{o_get<r + 0>() * inv, o_get<r + 1>() * inv, o_get<r + 2>() * inv, o_get<r + 3>() * inv});
-    store_wt(dst + 32 * CB + 8, f32x4{o_get<r + 4>() * inv, o_get<r + 5>() * inv, o_get<r + 6>() * inv, o_get<r + 7>() * inv});
-    store_wt(dst + 32 * CB + 16,
-             f32x4{o_get<r + 8>() * inv, o_get<r + 9>() * inv, o_get<r + 10>() * inv, o_get<r + 11>() * inv});
-    store_wt(dst + 32 * CB + 24,
-             f32x4{o_get<r + 12>() * inv, o_get<r + 13>() * inv, o_get<r + 14>() * inv, o_get<r + 15>() * inv});
-    o8_store_rec<CB + 1>(dst, inv);
+// The epilogue stages each wave's 32 rows through LDS (its own 36 KB stage,
+// rows kStageRow8 bytes apart: the 16-byte pad puts the 32 rows of one write
+// in distinct banks) so that every global store writes 1 KB of one row; stored
+// straight from the 32x32 layout, a store would write 32 bytes of 32 rows.
+constexpr int kStageRow8 = 1024 + 16;
+
+// fp32 output, half H (columns 256H .. 256H+255): block cb, register quad i
+// holds columns 32cb + 8i + 4(l/32) .. +3; `row` is this lane's row base
+// in the stage plus 16(l/32).
+template <int H, int CB>
+__device__ __forceinline__ void o8_stage_f32_rec(uint32_t row, float inv) {
+  if constexpr (CB < 8) {
+    constexpr int r = 16 * (8 * H + CB);
+    *LDS_AS(f32x4, (uintptr_t)(row + 128 * CB + 0)) =
+        f32x4{o_get<r + 0>() * inv, o_get<r + 1>() * inv, o_get<r + 2>() * inv, o_get<r + 3>() * inv};
+    *LDS_AS(f32x4, (uintptr_t)(row + 128 * CB + 32)) =
+        f32x4{o_get<r + 4>() * inv, o_get<r + 5>() * inv, o_get<r + 6>() * inv, o_get<r + 7>() * inv};
+    *LDS_AS(f32x4, (uintptr_t)(row + 128 * CB + 64)) =
+        f32x4{o_get<r + 8>() * inv, o_get<r + 9>() * inv, o_get<r + 10>() * inv, o_get<r + 11>() * inv};
+    *LDS_AS(f32x4, (uintptr_t)(row + 128 * CB + 96)) =
+        f32x4{o_get<r + 12>() * inv, o_get<r + 13>() * inv, o_get<r + 14>() * inv, o_get<r + 15>() * inv};
+    o8_stage_f32_rec<H, CB + 1>(row, inv);
   }
 }
 
@@ -210,9 +219,9 @@ __device__ __forceinline__ void o8_store_rec(float* dst, float inv) {
 // block c and 16-lane group grp of that kernel): here column
 // 32cb + 8i + 4g + j sits at 32cb + 16(i%2) + 8g + 4(i/2) + j, so register
 // quads 0 and 2 of a block form 8 consecutive positions, and so do 1 and 3
-// (dst already points at position 8g of the row).
+// (`row` is this lane's row base in the stage plus 16(l/32)).
 template <int CB>
-__device__ __forceinline__ void o8_store_half_rec(_Float16* dst, float c) {
+__device__ __forceinline__ void o8_stage_half_rec(uint32_t row, float c) {
   if constexpr (CB < 16) {
     typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
     constexpr int r = 16 * CB;
@@ -222,9 +231,9 @@ __device__ __forceinline__ void o8_store_half_rec(_Float16* dst, float c) {
     f16x8 w1 = {(_Float16)(o_get<r + 4>() * c), (_Float16)(o_get<r + 5>() * c), (_Float16)(o_get<r + 6>() * c),
                 (_Float16)(o_get<r + 7>() * c), (_Float16)(o_get<r + 12>() * c), (_Float16)(o_get<r + 13>() * c),
                 (_Float16)(o_get<r + 14>() * c), (_Float16)(o_get<r + 15>() * c)};
-    store_wt(dst + 32 * CB, w0);
-    store_wt(dst + 32 * CB + 16, w1);
-    o8_store_half_rec<CB + 1>(dst, c);
+    *LDS_AS(f16x8, (uintptr_t)(row + 64 * CB)) = w0;
+    *LDS_AS(f16x8, (uintptr_t)(row + 64 * CB + 32)) = w1;
+    o8_stage_half_rec<CB + 1>(row, c);
   }
 }
 
@@ -726,16 +735,28 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     if (bad_len) lse_v = NAN;
     // O holds sum_t p_t 2^(e_t - e0 + 6) codes_t = 2^(133 - e0) sum_t p_t V_t.
     const int oexp = e0 - 127 - kWeightExp8;
+    // Every wave is past its last LDS read of the piece (and its copies have
+    // landed): the stages are free for staging, wave w using stage w.
+    __syncthreads();
+    const uint32_t stg = lds_addr(smem + wave * kStageBytes8);
+    const uint32_t stg_row = stg + l32 * kStageRow8 + 16 * g;
+    const int nrow = min(32, rows - wave_row0);  // rows of this wave to store
     if (sg.partial < 0) {
       float inv = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, oexp) : 0.f;
       if (bad_len) inv = NAN;
-      if (row_ok) {
-        int r = row;
-        asm volatile("" : "+v"(r));
-        const int64_t oi = (int64_t)b * rows + r;
-        o8_store_rec<0>(out + oi * 512 + 4 * g, inv);
-        if (g == 0) lse[oi] = lse_v;
+      float* obase = out + ((int64_t)b * rows + wave_row0) * 512 + 4 * lane;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 0)
+          o8_stage_f32_rec<0, 0>(stg_row, inv);
+        else
+          o8_stage_f32_rec<1, 0>(stg_row, inv);
+        for (int r = 0; r < nrow; ++r) {
+          const f32x4 v = *LDS_AS(const f32x4, (uintptr_t)(stg + r * kStageRow8 + 16 * lane));
+          store_wt(obase + (int64_t)r * 512 + 256 * h, v);
+        }
       }
+      if (row_ok && g == 0) lse[(int64_t)b * rows + row] = lse_v;
     } else {
       const int64_t slot = (int64_t)sg.partial * nrb + rb;
       float amax = pair_max(o8_absmax_rec<0>(0.f));
@@ -743,14 +764,17 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       const float c = __builtin_ldexpf(1.f, 15 - e);
       float f = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, e - 15 + oexp) : 0.f;
       if (bad_len) f = NAN;
-      if (row_ok) {
+      o8_stage_half_rec<0>(stg_row, c);
+      typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+      _Float16* hbase = reinterpret_cast<_Float16*>(ws_o) + (slot * kRowsPerBlock8 + wave * 32) * 512 + 8 * lane;
+      for (int r = 0; r < nrow; ++r) {
+        const f16x8 v = *LDS_AS(const f16x8, (uintptr_t)(stg + r * kStageRow8 + 16 * lane));
+        store_wt(hbase + (int64_t)r * 512, v);
+      }
+      if (row_ok && g == 0) {
         const int64_t ri = slot * kRowsPerBlock8 + row_local;
-        _Float16* dst = reinterpret_cast<_Float16*>(ws_o) + ri * 512 + 8 * g;
-        o8_store_half_rec<0>(dst, c);
-        if (g == 0) {
-          ws_lse[ri] = lse_v;
-          ws_f[ri] = f;
-        }
+        ws_lse[ri] = lse_v;
+        ws_f[ri] = f;
       }
     }
   }
