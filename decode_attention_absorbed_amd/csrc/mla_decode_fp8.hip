@@ -67,6 +67,14 @@ constexpr int kLoadsPerWave8 = kStageBytes8 / 1024 / kWaves8;  // 9 one-KB copie
 constexpr int kCopiesPerWave8 = kLoadsPerWave8 + 1;            // + the scale bytes
 constexpr int kScaleArea8 = 256;                          // one wave's copy of a tile's scale bytes
 constexpr int kKSteps8 = 576 / 64;                        // 9 K steps of QK^T
+#ifndef MLA8_QK_DEPTH
+#define MLA8_QK_DEPTH 1
+#endif
+#ifndef MLA8_PV_DEPTH
+#define MLA8_PV_DEPTH 1
+#endif
+constexpr int kQkDepth8 = MLA8_QK_DEPTH;  // MFMAs of K-operand reads in flight ahead
+constexpr int kPvDepth8 = MLA8_PV_DEPTH;  // column blocks of V^T reads in flight ahead
 constexpr int kWeightExp8 = 6;                            // P is scaled by 2^6 before rounding
 constexpr float kRefStep8 = 32.0f;                        // reference moves past this (log2 units)
 constexpr float kLn2_8 = 0.69314718055994530942f;
@@ -545,20 +553,22 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     auto qk_tile = [&](int stage, f32x16(&acc)[2], auto&& extra) {
       const uint32_t base = lds_addr(smem + stage * kStageBytes8);
       // MFMA m = 2s + kb; its operand is read one MFMA ahead.
-      i32x8 a[2];
+      constexpr int D = kQkDepth8;
+      i32x8 a[D + 1];
       auto read = [&](int m, i32x8& dst) {
         const uint32_t o = base + 18432 * (m & 1) + 2048 * (m >> 1);
         const f32x4 lo = *LDS_AS(const f32x4, (uintptr_t)(o + qk_off0));
         const f32x4 hi = *LDS_AS(const f32x4, (uintptr_t)(o + qk_off1));
         dst = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      read(0, a[0]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) read(d, a[d]);
       static_for<2 * kKSteps8>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int s = m >> 1, kb = m & 1;
-        if constexpr (m + 1 < 2 * kKSteps8) read(m + 1, a[(m + 1) & 1]);
+        if constexpr (m + D < 2 * kKSteps8) read(m + D, a[(m + D) % (D + 1)]);
         extra(m);
-        s_mfma8(acc[kb], a[m & 1], q8[s], ea[kb], qsc[s], s == 0);
+        s_mfma8(acc[kb], a[m % (D + 1)], q8[s], ea[kb], qsc[s], s == 0);
         __builtin_amdgcn_sched_barrier(0);
       });
       s_mfma8_drain(acc);
@@ -578,13 +588,15 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     };
     const int one_e8m0 = 127;  // V^T is not scaled
     auto pv_tile = [&](int stage, const i32x8& pt, int pscale, auto&& extra) {
-      i32x8 v[2];
-      read_v(stage, 0, v[0]);
+      constexpr int DV = kPvDepth8;
+      i32x8 v[DV + 1];
+#pragma unroll
+      for (int d = 0; d < DV; ++d) read_v(stage, d, v[d]);
       static_for<16>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
-        if constexpr (cb + 1 < 16) read_v(stage, cb + 1, v[(cb + 1) & 1]);
+        if constexpr (cb + DV < 16) read_v(stage, cb + DV, v[(cb + DV) % (DV + 1)]);
         extra(cb);
-        OBlock8<cb>::mfma(v[cb & 1], pt, one_e8m0, pscale);
+        OBlock8<cb>::mfma(v[cb % (DV + 1)], pt, one_e8m0, pscale);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
