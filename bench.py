@@ -38,12 +38,19 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode attention TFLOP/s + HBM GB/s (% of roofline), H=128, 576-d latent"
 
 
-def kernel_sha() -> str:
-    """Hash of the kernel sources: counters taken for another build are stale."""
+#: the sources each decode kernel is built from (its file and what it includes)
+KERNEL_SOURCES = {
+    "bf16": ["mla_decode.hip", "device_common.h", "agpr_tiles.inc", "plan_internal.h", "decode_fp8.h"],
+    "fp8": ["mla_decode_fp8.hip", "device_common.h", "agpr_tiles.inc", "agpr_tiles_fp8.inc", "plan_internal.h",
+            "decode_fp8.h"],
+}
+
+
+def kernel_sha(kv: str = "bf16") -> str:
+    """Hash of one decode kernel's sources: counters taken for another build are stale."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "decode_attention_absorbed_amd", "csrc", "*"))):
-        if p.endswith((".hip", ".cpp", ".h", ".inc")):
-            h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES[kv]:
+        h.update(open(os.path.join(ROOT, "decode_attention_absorbed_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -51,14 +58,14 @@ def traffic_name(config: str, kv: str) -> str:
     return config if kv == "bf16" else f"{config}_{kv}"
 
 
-def load_traffic(config: str, per_launch_bytes_alg: int):
+def load_traffic(config: str, kv: str):
     """HBM bytes per decode launch measured with rocprofv3 counters (see
     profiles/), or None if missing or taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{traffic_name(config, kv)}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel_sha") != kernel_sha(kv):
         return None
     return t.get("decode_bytes_per_launch")
 
@@ -116,7 +123,7 @@ def traffic_from(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     cwrite = _counter_per_dispatch(write_dir, "WRITE_SIZE", "combine_kernel")
     res = {
         "config": config,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha("fp8" if config.endswith("_fp8") else "bf16"),
         "copy_bytes": COPY_BYTES,
         "copy_fetch_kib": cf_k,
         "copy_write_kib": cw_k,
@@ -271,7 +278,7 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
     else:
         achieved = flops / (dec_burst * 1e-3) / 1e12
         peak, unit = (acc.PEAK_FP8_FLOPS if fp8 else acc.PEAK_BF16_FLOPS) / 1e12, "TFLOP/s"
-    traffic = load_traffic(traffic_name(config, kv), nbytes)
+    traffic = load_traffic(config, kv)
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -319,7 +326,7 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
         "input_copies": copies,
         "num_workgroups": plan.query(bnd.MLA_Q_NUM_WORKGROUPS),
         "num_partials": plan.query(bnd.MLA_Q_NUM_PARTIALS),
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(kv),
     }
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline(x, cpu_seconds)
