@@ -613,30 +613,53 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     float mx = 0.f, mu_t = 0.f, px = 1.f;
     int psc = 127;  // PV scale byte of the tile in flight
     // Softmax of one tile of scores s (s[kb][4a + b] = key tb_s + 32kb + 8a +
-    // 4g + b of this lane's row), in kSmSteps8 steps spread between MFMAs:
-    //   0-1: mask block kb's keys past the row's limit (tiles that need it),
-    //   2: the lane's max, 3: the row max (lane pair), reference and x,
-    //   4-11: a = step - 4 (kb = a / 4): p = 2^(s*scale - mu - x), running
-    //         sum p 2^x, P' = p * sc, and the E4M3 word of P^T (K slots
-    //         4(4kb + a%4)..).
-    constexpr int kSmSteps8 = 12;
+    // 4g + b of this lane's row), in kSmSteps8 steps, one per PV MFMA gap:
+    //   0: mask the keys past the row's limit (tiles that need it), lane max;
+    //   1: row max (lane pair), reference and x; the LDS reads of the first
+    //      two key groups' factors sc;
+    //   2, 3: element pairs 0-1 and 2-3; 4..15: pair `step` (pair j = elements
+    //      2(j%2), 2(j%2)+1 of key group j/2, group q = (kb, a) = (q/4, q%4)):
+    //      p = 2^(s*scale - mu - x), running sum p 2^x, P' = p * sc, and half a
+    //      word of P^T (K slots 4(4kb + a) ..).  The factors of group q are read
+    //      two groups ahead into sc_buf[q % 2].
+    constexpr int kSmSteps8 = 16;
+    f32x4 sc_buf[2];
+    auto sc_read = [&](int q) {
+      const int kb = q >> 2, a = q & 3;
+      sc_buf[q & 1] = *LDS_AS(const f32x4, (uintptr_t)(sc_base + 4 * (32 * kb + 8 * a + 4 * g)));
+    };
+    auto sm_pair = [&](int j, f32x16(&s)[2], i32x8& pt) {
+      const int q = j >> 1, h = j & 1, kb = q >> 2, a = q & 3;
+      const f32x4& sc = sc_buf[q & 1];
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * a + 2 * h], scale_log2, -mu_t));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * a + 2 * h + 1], scale_log2, -mu_t));
+      l_part = __builtin_fmaf(p0, px, l_part);
+      l_part = __builtin_fmaf(p1, px, l_part);
+      if (h)
+        pt[4 * kb + a] = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * sc[2], p1 * sc[3], pt[4 * kb + a], true);
+      else
+        pt[4 * kb + a] = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * sc[0], p1 * sc[1], 0, false);
+      if (h == 1 && q + 2 < 8) sc_read(q + 2);
+    };
     auto softmax_step = [&](int step, f32x16(&s)[2], bool need_mask, int tb_s, i32x8& pt, int& pscale) {
-      if (step < 2) {
-        const int kb = step;
+      if (step == 0) {
         if (__builtin_amdgcn_readfirstlane((int)need_mask)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = tb_s + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            s[kb][r] = tok < lim ? s[kb][r] : -INFINITY;
-          }
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int tok = tb_s + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+              s[kb][r] = tok < lim ? s[kb][r] : -INFINITY;
+            }
         }
-      } else if (step == 2) {
         float m0 = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[0][4], s[0][5]), max3(s[0][6], s[0][7], s[0][8]));
         float m1 = max3(max3(s[0][9], s[0][10], s[0][11]), max3(s[0][12], s[0][13], s[0][14]), max3(s[0][15], s[1][0], s[1][1]));
         float m2 = max3(max3(s[1][2], s[1][3], s[1][4]), max3(s[1][5], s[1][6], s[1][7]), max3(s[1][8], s[1][9], s[1][10]));
         float m3 = max3(max3(s[1][11], s[1][12], s[1][13]), s[1][14], s[1][15]);
         mx = max3(m0, m1, max3(m2, m3, m3));
-      } else if (step == 3) {
+      } else if (step == 1) {
+        sc_read(0);
+        sc_read(1);
         mx = pair_max(mx);
         const float m = mx * scale_log2;
         const bool fin = m > kMuFloor8;
@@ -657,18 +680,11 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         mu_t = mu + (float)x;
         px = __builtin_ldexpf(1.f, x);
         pscale = 127 + x + de;
+      } else if (step < 4) {
+        sm_pair(2 * (step - 2), s, pt);
+        sm_pair(2 * (step - 2) + 1, s, pt);
       } else if (step < kSmSteps8) {
-        const int q = step - 4, kb = q >> 2, a = q & 3;
-        const f32x4 sc = *LDS_AS(const f32x4, (uintptr_t)(sc_base + 4 * (32 * kb + 8 * a + 4 * g)));
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * a + j], scale_log2, -mu_t));
-          l_part = __builtin_fmaf(p[j], px, l_part);
-        }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * sc[0], p[1] * sc[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * sc[2], p[3] * sc[3], w, true);
-        pt[4 * kb + a] = w;
+        sm_pair(step, s, pt);
       }
     };
 
@@ -723,7 +739,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       if (has_next) {
         const bool nm = tb + 2 * kTile8 > lim_wave;
         pv_tile(st_cur, pt, psc, [&](int cb) {
-          if (cb >= 2 && cb - 2 < kSmSteps8) softmax_step(cb - 2, s_next, nm, tb + kTile8, pt_next, psc_next);
+          softmax_step(cb, s_next, nm, tb + kTile8, pt_next, psc_next);
         });
         if (__any(any_scale)) {
           o8_drain();
