@@ -148,3 +148,68 @@ def test_plan_query_keys(host_plan):
     assert host_plan.query(bnd.MLA_Q_ROWS_PER_BLOCK) in (64, 128)
     assert host_plan.query(bnd.MLA_Q_TILE_TOKENS) in (32, 64)
     assert host_plan.query(999) == -1
+
+
+# ---- the FP8 entry points: the same host-side checks --------------------------------------
+
+
+def _call8(plan, **over):
+    f = _Fake()
+    a = dict(
+        q=f(), qp=f(), codes=f(), scales=f(), num_pages=100, bt=f(), bt_stride=64, lens=f(),
+        scale=1 / math.sqrt(192), out=f(), lse=f(), ws=f(), ws_bytes=plan.workspace_bytes, stream=None,
+    )
+    a.update(over)
+    return mla.lib().mla_decode_fp8(
+        plan.handle, a["q"], a["qp"], a["codes"], a["scales"], a["num_pages"], a["bt"], a["bt_stride"], a["lens"],
+        a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"],
+    )
+
+
+@pytest.fixture(scope="module")
+def host_plan8():
+    p = bnd.mla_decode_fp8_plan_host([4000, 17], 1, 128, 64, 64)
+    assert p.workspace_bytes > 0
+    assert p.query(bnd.MLA_Q_TILE_TOKENS) == 64 and p.query(bnd.MLA_Q_ROWS_PER_BLOCK) == 128
+    yield p
+    p.destroy()
+
+
+def test_fp8_decode_rejects_null_pointers(host_plan8):
+    for k in ("q", "qp", "codes", "scales", "bt", "lens", "out", "lse"):
+        assert _call8(host_plan8, **{k: None}) == 1, k
+
+
+def test_fp8_decode_rejects_misalignment(host_plan8):
+    for k in ("q", "qp", "codes", "out"):
+        assert _call8(host_plan8, **{k: (1 << 40) + 8}) == 1, k
+    assert _call8(host_plan8, scales=(1 << 40) + 2) == 1
+    assert _call8(host_plan8, ws=(1 << 40) + 128) == 1
+
+
+def test_fp8_decode_rejects_bad_sizes(host_plan8):
+    assert _call8(host_plan8, num_pages=0) == 1
+    assert _call8(host_plan8, bt_stride=62) == 1
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert _call8(host_plan8, scale=s) == 1, s
+    assert _call8(host_plan8, ws_bytes=host_plan8.workspace_bytes - 1) == 3
+
+
+def test_plan_kinds_are_not_interchangeable(host_plan, host_plan8):
+    # each decode call refuses the other kind's plan before anything else
+    assert _call8(host_plan) == 1
+    assert "mla_decode_fp8_plan" in mla.lib().mla_last_error().decode()
+    assert _call(host_plan8) == 1
+    assert "mla_decode_plan" in mla.lib().mla_last_error().decode()
+
+
+def test_fp8_plan_covers_every_key_once():
+    lens = [2, 63, 64, 65, 4000, 20480]
+    p = bnd.mla_decode_fp8_plan_host(lens, 2, 128, 16, 256)
+    seg = p.segments()
+    for b, L in enumerate(lens):
+        pieces = sorted((int(s[1]), int(s[2])) for s in seg if s[0] == b)
+        assert pieces[0][0] == 0 and pieces[-1][1] == L
+        assert all(pieces[i][1] == pieces[i + 1][0] for i in range(len(pieces) - 1))
+        assert all(lo % 64 == 0 for lo, _ in pieces)  # pieces start on 64-key tiles
+    p.destroy()
