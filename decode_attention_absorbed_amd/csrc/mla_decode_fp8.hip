@@ -674,8 +674,10 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         l_part *= alpha;
         alpha_o = alpha * e_alpha;
         any_scale = any_scale || (had && (alpha != 1.f || e_moved));
-        // x = floor(m - mu), with x + de kept inside the E8M0 range
-        int x = fin ? (int)__builtin_floorf(m - mu) : 0;
+        // x = floor(m - mu) (m - mu >= -2^9 before the conversion: a tile far
+        // below the reference has weights that round to zero anyway), with
+        // x + de kept inside the E8M0 range
+        int x = fin ? (int)__builtin_floorf(fmaxf(m - mu, -512.f)) : 0;
         x = min(max(x + de, -127), 127) - de;
         mu_t = mu + (float)x;
         px = __builtin_ldexpf(1.f, x);

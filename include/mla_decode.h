@@ -184,10 +184,12 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse,
  *             integer with max|q| * 2^-f <= 448, limited to [-127, 127],
  *             codes = round-to-nearest-even of q * 2^-f (saturated at 448).
  *
- * The softmax weights are rounded to E4M3 for the PV product (the row's
- * largest weight scaled into [64, 256]); the output therefore carries a
+ * The softmax weights are rounded to E4M3 for the PV product (each tile's
+ * largest weight scaled into [64, 128)); the output therefore carries a
  * relative error of a few percent of the weights' rounding, averaged over
- * the keys; lse is unaffected.
+ * the keys; lse is unaffected.  Scores (softmax_scale * q . k) must stay
+ * below ~2^19 in magnitude, where fp32 still resolves their differences
+ * (per-token scales allow far larger values; results are then not defined).
  *
  * mla_decode_fp8_plan / _plan_host: as mla_decode_plan / _plan_host, for the
  *   FP8 kernel (64-key tiles).  A plan of one kind is refused by the other

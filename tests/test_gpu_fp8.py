@@ -2,7 +2,8 @@
 
 Tolerance, derived from the arithmetic (the oracle module states the model):
 the scores use the same E4M3 query codes and exactly scaled keys on both sides,
-so lse differs only by fp32 rounding (bar: max-abs <= 1e-3, as for bf16).  The
+so lse differs only by fp32 rounding (bar: max-abs <= 1e-3, as for bf16, or the
+worst-case rounding of a 576-term fp32 sum where scores are large).  The
 output differs mainly because the kernel rounds the softmax weights to E4M3
 before the PV product; ``fp8_weight_error_rms`` gives the root-mean-square
 size of that error per element.  Bars: the L2 norm of the error is at most
@@ -18,7 +19,13 @@ torch = pytest.importorskip("torch")
 
 import decode_attention_absorbed_amd as mla  # noqa: E402
 from decode_attention_absorbed_amd import binding as bnd  # noqa: E402
-from oracle import dequantize_cache, fp8_weight_error_rms, mla_decode_fp8_ref  # noqa: E402
+from oracle import (  # noqa: E402
+    dequantize_cache,
+    dequantize_query,
+    fp8_weight_error_rms,
+    mla_decode_fp8_ref,
+    quantize_query,
+)
 from workloads import (  # noqa: E402
     make_config_fp8,
     make_inputs_fp8,
@@ -55,10 +62,27 @@ def oracle(x, idx=None):
     args = (x.q_nope_f64()[idx], x.q_pe_f64()[idx], x.cache_codes, x.cache_exps, x.block_table[idx], x.seq_lens[idx], x.softmax_scale)
     o, l = mla_decode_fp8_ref(*args)
     rms = fp8_weight_error_rms(*args)
-    return o, l, rms
+    return o, l, rms, score_abs_max(x, idx)
 
 
-def compare(out, lse, ref_o, ref_l, rms, what=""):
+def score_abs_max(x, idx):
+    """Per row, scale * max_t sum_i |q_i k_ti| over its visible keys: the size
+    of the terms the fp32 score sums add up (their rounding scales with it)."""
+    codes, f = quantize_query(x.q_nope_f64()[idx], x.q_pe_f64()[idx])
+    q = np.abs(dequantize_query(codes, f))
+    cache = np.abs(dequantize_cache(x.cache_codes, x.cache_exps))
+    out = np.zeros(q.shape[:-1])
+    for i, b in enumerate(idx):
+        L = int(x.seq_lens[b])
+        t = np.arange(L)
+        K = cache[x.block_table[b, t // x.page], t % x.page]
+        for j in range(x.q_len):
+            n = L - x.q_len + 1 + j
+            out[i, j] = x.softmax_scale * (q[i, j] @ K[:n].T).max(axis=-1)
+    return out
+
+
+def compare(out, lse, ref_o, ref_l, rms, s_abs, what=""):
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)), f"{what}: non-finite output"
     err = out - ref_o
     e_l = float(np.max(np.abs(lse - ref_l)))
@@ -70,7 +94,11 @@ def compare(out, lse, ref_o, ref_l, rms, what=""):
         f"| worst element / bar {worst:.3f} | lse max-abs {e_l:.3e}",
         flush=True,
     )
-    assert e_l <= LSE_MAX_ABS, f"{what}: lse max-abs {e_l}"
+    # lse: 1e-3, or the worst-case rounding of a 576-term fp32 score sum,
+    # 576 * 2^-24 of the sum of the terms' magnitudes, where scores are large
+    # (|d lse| <= max_t |d s_t|)
+    bar_l = np.maximum(LSE_MAX_ABS, 576 * 2.0**-24 * s_abs)
+    assert np.all(np.abs(lse - ref_l) <= bar_l), f"{what}: lse max-abs {e_l}"
     assert ratio <= RMS_FACTOR, f"{what}: error L2 is {ratio:.2f}x the model's"
     assert worst <= 1.0, f"{what}: an element is {worst:.2f}x past its bar"
 
@@ -153,7 +181,7 @@ def test_fp8_nan_tails_and_unreferenced_pages_never_reach_the_output(dev):
 def test_fp8_single_visible_key_returns_its_latent_row(dev):
     x = make_inputs_fp8(2, 128, 1, 16, [1, 1], seed=34)
     out, lse = run_gpu(x, dev)
-    ref_o, ref_l, _ = oracle(x)
+    ref_o, ref_l, _, _ = oracle(x)
     cache = dequantize_cache(x.cache_codes, x.cache_exps)
     for b in range(2):
         row = cache[x.block_table[b, 0], 0, :512]
@@ -181,3 +209,34 @@ def test_fp8_plan_and_kernel_kinds_do_not_mix(dev):
     cache_bf16 = torch.zeros((x.num_pages, 16, 576), dtype=torch.bfloat16, device=dev)
     with pytest.raises(bnd.MLAError):
         mla.mla_decode(p8, t["q_nope"], t["q_pe"], cache_bf16, t["block_table"], t["seq_lens"], 0.1)
+
+
+def _pages_of(x, b, t0, t1):
+    """(page, slot) pairs of keys t0 .. t1-1 of request b."""
+    t = np.arange(t0, t1)
+    return x.block_table[b, t // x.page], t % x.page
+
+
+def test_fp8_row_reference_moves_and_output_rescales(dev):
+    # Keys from 256 on get 8x larger scale bytes' worth (+3): their scores
+    # dwarf the first tiles' by far more than 2^32 in log2 units, so every
+    # row's reference moves mid-piece and the accumulated output is rescaled.
+    x = make_inputs_fp8(2, 128, 1, 64, [600, 450], seed=41)
+    for b, L in enumerate(x.seq_lens):
+        pg, sl = _pages_of(x, b, 256, int(L))
+        x.cache_exps[pg, sl] += 3
+    out, lse = run_gpu(x, dev, num_cus=1)  # one piece per request: the moves happen inside it
+    compare(out, lse, *oracle(x), what="reference moves")
+
+
+def test_fp8_scale_reference_moves(dev):
+    # The first tile's scale bytes sit 70 below the rest (more than the 2^64
+    # the PV scale operand may carry between tiles): when the second tile
+    # arrives, the kernel's scale reference moves and the output accumulated
+    # so far is rescaled.  Scores stay moderate (the first tile's are ~0).
+    x = make_inputs_fp8(2, 64, 1, 64, [400, 130], seed=43)
+    for b in range(2):
+        pg, sl = _pages_of(x, b, 0, 64)
+        x.cache_exps[pg, sl] = (x.cache_exps[pg, sl].astype(np.int32) - 70).astype(np.uint8)
+    out, lse = run_gpu(x, dev, num_cus=1)
+    compare(out, lse, *oracle(x), what="scale reference moves")
