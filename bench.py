@@ -340,7 +340,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long")
+    ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long | mtp4 | mtp8")
     ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,7 +358,7 @@ def main() -> int:
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.all:
-        for name in ["tiny", "dsv3", "mtp", "mixed", "long"]:
+        for name in ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"]:
             r = run(name, args.steps, args.warmup, False, 0.0, args.kv)
             print(json.dumps(r), file=sys.stderr, flush=True)
     res = run(args.config, args.steps, args.warmup, not args.no_cpu_baseline and args.kv == "bf16", args.cpu_seconds,

@@ -133,10 +133,11 @@ def test_fp8_forced_split_counts(dev, num_cus):
     compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
 
 
-SAMPLES = {"tiny": None, "dsv3": [0, 31], "mtp": "extremes", "mixed": "mixed", "long": None}
+SAMPLES = {"tiny": None, "dsv3": [0, 31], "mtp": "extremes", "mixed": "mixed", "long": None,
+           "mtp4": "extremes", "mtp8": "extremes"}
 
 
-@pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp", "mixed", "long"])
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"])
 def test_fp8_named_workload_parity(dev, name):
     x = make_config_fp8(name)
     print(f"{name}: B={x.batch} H={x.heads} q_len={x.q_len} pages={x.num_pages}", flush=True)

@@ -214,3 +214,16 @@ def test_out_of_range_page_ids_read_page_zero(dev):
     t_bt = torch.from_numpy(bt).to(dev)
     out, lse = run_gpu(x, dev, block_table=t_bt)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+# ---- more draft tokens (q_len 4 and 8 at full head count), sampled requests --------------
+
+
+@pytest.mark.parametrize("name", ["mtp4", "mtp8"])
+def test_long_draft_workloads(dev, name):
+    x = make_config(name)
+    out, lse = run_gpu(x, dev)
+    idx = [int(np.argmin(x.seq_lens)), int(np.argmax(x.seq_lens))]
+    ref_o, ref_l = oracle(x, idx)
+    compare(out[idx], lse[idx], ref_o, ref_l, what=f"{name} requests {idx}")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))

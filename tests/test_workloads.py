@@ -24,6 +24,10 @@ def test_named_workload_structure():
     assert config_lens("long").tolist() == [131072]
     assert config_lens("dsv3").tolist() == [4096] * 32
     assert sorted(config_lens("tiny").tolist()) == [37, 100]
+    for name, B, q in (("mtp4", 32, 4), ("mtp8", 16, 8)):
+        L = config_lens(name)
+        assert len(L) == B and L.min() >= 1024 and L.max() <= 8192
+        assert B * q * CONFIGS[name]["heads"] == 64 * 2 * 128  # the same query rows as "mtp"
 
 
 def test_block_table_is_a_permutation_dealt_in_order():
@@ -40,4 +44,4 @@ def test_seeded_determinism():
     b = make_inputs(2, 4, 2, 16, [20, 33], seed=9)
     for f in ("q_nope", "q_pe", "cache", "block_table", "seq_lens"):
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
-    assert set(CONFIGS) == {"tiny", "dsv3", "mtp", "mixed", "long"}
+    assert set(CONFIGS) == {"tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"}

@@ -13,13 +13,15 @@ Workload shapes come from the pages:
   time model with its (576 + 512) x 128 terms; section 3.1.1 for the BF16
   KV cache).
 * One MTP draft token, i.e. two query tokens per request (same report,
-  section 5.3 and the x2 factor in section 7.2).
+  section 5.3 and the x2 factor in section 7.2); 3 and 7 draft tokens for
+  the longer-draft workloads (the CloudMatrix384 digest's serving setup
+  speculates several tokens ahead).
 * A mixed batch of 20K-token (40%) and 400-token (60%) requests (Ascend
   troubleshooting note on decode TPOT jitter, section 5.2, the random mixed
   data set).
 
 Generation recipe (fixed draw order, ``numpy.random.default_rng(seed)``):
-  1. sequence lengths (only config "mtp" draws them),
+  1. sequence lengths (only the "mtp" configs draw them),
   2. a shuffle of the request order,
   3. a permutation of all pages, dealt to the requests in order,
   4. q_nope_absorbed, 5. q_pe, 6. the paged cache;
@@ -46,8 +48,14 @@ CONFIGS: Dict[str, dict] = {
     # 40% of 64 = 25.6 requests, rounded to 26 long and 38 short.
     "mixed": dict(seed=4, batch=64, heads=128, q_len=1, page=64, lens=[20480] * 26 + [400] * 38),
     "long": dict(seed=5, batch=1, heads=128, q_len=1, page=64, lens=[131072]),
+    # More draft tokens (3 and 7 drafts: 4 and 8 query tokens per request),
+    # the same 16384 query rows as "mtp" over fewer requests.
+    "mtp4": dict(seed=6, batch=32, heads=128, q_len=4, page=64, lens=("uniform", 1024, 8192)),
+    "mtp8": dict(seed=7, batch=16, heads=128, q_len=8, page=64, lens=("uniform", 1024, 8192)),
 }
 CONFIG_ORDER = ["tiny", "dsv3", "mtp", "mixed", "long"]
+#: workloads beyond the five headline ones (more draft tokens)
+EXTRA_CONFIGS = ["mtp4", "mtp8"]
 
 
 def softmax_scale_default() -> float:
