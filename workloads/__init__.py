@@ -389,3 +389,62 @@ def poison_unreferenced_fp8(x: MLAInputsFP8) -> None:
         ref[x.block_table[b, :n]] = True
     x.cache_codes[~ref] = 0x7F
     x.cache_exps[~ref] = 255
+
+
+# ---------------------------------------------------------------------------
+# Prolog / epilog inputs (the steps around the decode attention)
+# ---------------------------------------------------------------------------
+ROPE_THETA = 10000.0
+
+
+@dataclass
+class PrologInputs:
+    """One decode step's inputs to the prolog and the weights of the epilog.
+
+    bf16 tensors as raw uint16 bits; the RoPE table as float32."""
+
+    batch: int
+    q_len: int
+    heads: int
+    seq_lens: np.ndarray  # int32 [B] (the q_len new tokens included)
+    q_nope128: np.ndarray  # uint16 [B, q_len, H, 128]
+    q_pe_raw: np.ndarray  # uint16 [B, q_len, H, 64]
+    w_uk_t: np.ndarray  # uint16 [H, 512, 128]: element [h, c, d] = W_UK[h][d][c]
+    c_kv_raw: np.ndarray  # uint16 [B, q_len, 512]
+    kv_norm_w: np.ndarray  # uint16 [512]
+    k_pe_raw: np.ndarray  # uint16 [B, q_len, 64]
+    rope_cos_sin: np.ndarray  # float32 [max_pos, 64]: cos of the 32 pair angles, then their sin
+    w_uv: np.ndarray  # uint16 [H, 128, 512]
+    rms_eps: float = 1e-6
+
+    def w_uk_f64(self) -> np.ndarray:
+        """W_UK [H, 128, 512] as float64."""
+        return np.ascontiguousarray(bf16_bits_to_f64(self.w_uk_t).transpose(0, 2, 1))
+
+
+def rope_cos_sin_table(max_pos: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """Plain RoPE constants of the model, [max_pos, 64] float32: pair i of
+    position p turns by p * theta^(-2i/64); cos of the 32 angles, then sin."""
+    inv = theta ** (-np.arange(0, D_ROPE, 2, dtype=np.float64) / D_ROPE)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_prolog_inputs(batch: int, q_len: int, heads: int, seq_lens: Sequence[int], seed: int) -> PrologInputs:
+    """Draw order: q_nope (128 wide), q_pe, W_UK^T, c_kv, the norm weight, k_pe,
+    W_UV; values N(0, 1) except the weights (N(0, 1/sqrt(fan-in))) and the
+    norm weight (1 + 0.1 N(0, 1)); all rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    n = lambda *s: rng.standard_normal(s, dtype=np.float32)
+    q_nope = to_bf16_bits(n(batch, q_len, heads, 128))
+    q_pe = to_bf16_bits(n(batch, q_len, heads, D_ROPE))
+    w_uk_t = to_bf16_bits(n(heads, D_LATENT, 128) / np.float32(np.sqrt(128.0)))
+    c_kv = to_bf16_bits(n(batch, q_len, D_LATENT))
+    w = to_bf16_bits(np.float32(1.0) + np.float32(0.1) * n(D_LATENT))
+    k_pe = to_bf16_bits(n(batch, q_len, D_ROPE))
+    w_uv = to_bf16_bits(n(heads, 128, D_LATENT) / np.float32(np.sqrt(float(D_LATENT))))
+    lens = np.asarray(seq_lens, np.int32)
+    return PrologInputs(
+        batch=batch, q_len=q_len, heads=heads, seq_lens=lens, q_nope128=q_nope, q_pe_raw=q_pe, w_uk_t=w_uk_t,
+        c_kv_raw=c_kv, kv_norm_w=w, k_pe_raw=k_pe, rope_cos_sin=rope_cos_sin_table(int(lens.max()) + 1), w_uv=w_uv,
+    )
