@@ -14,4 +14,6 @@ from .binding import (  # noqa: F401
     mla_decode_plan,
     mla_decode_plan_host,
     mla_decode_workspace_bytes,
+    mla_prolog,
+    mla_up_project,
 )

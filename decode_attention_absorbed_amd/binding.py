@@ -50,7 +50,13 @@ EXPORTED = (
     "mla_decode_fp8_plan_host",
     "mla_decode_fp8",
     "mla_decode_fp8_partials",
+    "mla_prolog",
+    "mla_up_project",
 )
+
+#: kv_format values of mla_prolog
+MLA_KV_BF16 = 0
+MLA_KV_FP8 = 1
 
 
 class MLAError(RuntimeError):
@@ -111,6 +117,13 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fp8.restype = ctypes.c_int
     L.mla_decode_fp8_partials.argtypes = L.mla_decode_fp8.argtypes
     L.mla_decode_fp8_partials.restype = ctypes.c_int
+    L.mla_prolog.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, ctypes.c_int32,
+        vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
+    ]
+    L.mla_prolog.restype = ctypes.c_int
+    L.mla_up_project.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
+    L.mla_up_project.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -337,3 +350,93 @@ def mla_decode_fp8(
         )
     )
     return out, lse
+
+
+def mla_prolog(
+    q_nope128: torch.Tensor,
+    q_pe_raw: torch.Tensor,
+    w_uk_t: torch.Tensor,
+    c_kv_raw: torch.Tensor,
+    kv_norm_w: torch.Tensor,
+    rms_eps: float,
+    k_pe_raw: torch.Tensor,
+    rope_cos_sin: torch.Tensor,
+    seq_lens: torch.Tensor,
+    block_table: torch.Tensor,
+    kv_cache: torch.Tensor,
+    kv_scales: Optional[torch.Tensor] = None,
+    q_nope_absorbed: Optional[torch.Tensor] = None,
+    q_pe: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue the prolog: absorbed query, RoPE'd q_pe, and the new tokens'
+    rows written into ``kv_cache`` (bf16 [num_pages, page, 576], or uint8 E4M3
+    codes with ``kv_scales`` uint8 [num_pages, page]); returns
+    (q_nope_absorbed, q_pe)."""
+    if q_nope128.dim() != 4 or q_nope128.shape[3] != 128:
+        raise ValueError(f"q_nope128: shape {tuple(q_nope128.shape)}, expected [B, q_len, H, 128]")
+    B, qlen, H = (int(v) for v in q_nope128.shape[:3])
+    dev = q_nope128.device
+    _expect(q_nope128, "q_nope128", torch.bfloat16, (B, qlen, H, 128))
+    _expect(q_pe_raw, "q_pe_raw", torch.bfloat16, (B, qlen, H, 64))
+    _expect(w_uk_t, "w_uk_t", torch.bfloat16, (H, 512, 128))
+    _expect(c_kv_raw, "c_kv_raw", torch.bfloat16, (B, qlen, 512))
+    _expect(kv_norm_w, "kv_norm_w", torch.bfloat16, (512,))
+    _expect(k_pe_raw, "k_pe_raw", torch.bfloat16, (B, qlen, 64))
+    if rope_cos_sin.dim() != 2 or rope_cos_sin.shape[1] != 64:
+        raise ValueError(f"rope_cos_sin: shape {tuple(rope_cos_sin.shape)}, expected [max_pos, 64]")
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, tuple(rope_cos_sin.shape))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table: shape {tuple(block_table.shape)}, expected [{B}, *]")
+    _expect(block_table, "block_table", torch.int32, tuple(block_table.shape))
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != 576:
+        raise ValueError(f"kv_cache: shape {tuple(kv_cache.shape)}, expected [num_pages, page, 576]")
+    fp8 = kv_cache.dtype == torch.uint8
+    _expect(kv_cache, "kv_cache", torch.uint8 if fp8 else torch.bfloat16, tuple(kv_cache.shape))
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an FP8 cache needs kv_scales")
+        _expect(kv_scales, "kv_scales", torch.uint8, tuple(kv_cache.shape[:2]))
+    if q_nope_absorbed is None:
+        q_nope_absorbed = torch.empty((B, qlen, H, 512), dtype=torch.bfloat16, device=dev)
+    if q_pe is None:
+        q_pe = torch.empty((B, qlen, H, 64), dtype=torch.bfloat16, device=dev)
+    _expect(q_nope_absorbed, "q_nope_absorbed", torch.bfloat16, (B, qlen, H, 512))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, qlen, H, 64))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(
+        lib().mla_prolog(
+            B, qlen, H,
+            _ptr(q_nope128), _ptr(q_pe_raw), _ptr(w_uk_t), _ptr(c_kv_raw), _ptr(kv_norm_w), float(rms_eps),
+            _ptr(k_pe_raw), _ptr(rope_cos_sin), int(rope_cos_sin.shape[0]),
+            _ptr(seq_lens), _ptr(block_table), int(block_table.shape[1]),
+            int(kv_cache.shape[0]), int(kv_cache.shape[1]), MLA_KV_FP8 if fp8 else MLA_KV_BF16,
+            _ptr(kv_cache), _ptr(kv_scales if fp8 else None),
+            _ptr(q_nope_absorbed), _ptr(q_pe), stream.cuda_stream,
+        )
+    )
+    return q_nope_absorbed, q_pe
+
+
+def mla_up_project(
+    attn_out: torch.Tensor,
+    w_uv: torch.Tensor,
+    o: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> torch.Tensor:
+    """Enqueue o[b, j, h] = W_UV[h] attn_out[b, j, h] (attn_out fp32 [B, q_len, H, 512],
+    w_uv bf16 [H, 128, 512]); returns o (bf16 [B, q_len, H, 128])."""
+    if attn_out.dim() != 4 or attn_out.shape[3] != 512:
+        raise ValueError(f"attn_out: shape {tuple(attn_out.shape)}, expected [B, q_len, H, 512]")
+    B, qlen, H = (int(v) for v in attn_out.shape[:3])
+    _expect(attn_out, "attn_out", torch.float32, (B, qlen, H, 512))
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, 128, 512))
+    if o is None:
+        o = torch.empty((B, qlen, H, 128), dtype=torch.bfloat16, device=attn_out.device)
+    _expect(o, "o", torch.bfloat16, (B, qlen, H, 128))
+    if stream is None:
+        stream = torch.cuda.current_stream(attn_out.device)
+    _check(lib().mla_up_project(B, qlen, H, _ptr(attn_out), _ptr(w_uv), _ptr(o), stream.cuda_stream))
+    return o

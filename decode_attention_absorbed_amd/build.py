@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["mla_decode.hip", "mla_decode_fp8.hip", "plan.cpp"]
+SOURCES = ["mla_decode.hip", "mla_decode_fp8.hip", "mla_prolog.hip", "plan.cpp"]
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

@@ -221,6 +221,60 @@ mla_status mla_decode_fp8_partials(const mla_plan* plan,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * The steps next to the decode attention.
+ *
+ * The Huawei report (section 6.1, the operators before MLA) absorbs the
+ * weights and fuses the decode prolog into one operator; the CloudMatrix384
+ * digest (its MLA optimization paragraph) names RMSNorm, the projections and
+ * RoPE as its parts; the report's decode flow (section 3.2.1) ends MLA with
+ * the output projection, whose input is the up-projected attention output.
+ *
+ * mla_prolog -- for the q_len new tokens of each request (positions
+ *   seq_lens[b] - q_len + j, j < q_len), enqueue on `stream`:
+ *     q_nope_absorbed[b, j, h] = W_UK[h]^T q_nope128[b, j, h]        (bf16, 512)
+ *     q_pe[b, j, h]            = RoPE(q_pe_raw[b, j, h])              (bf16, 64)
+ *     cache row of the token   = [RMSNorm(c_kv_raw[b, j]) * kv_norm_w | RoPE(k_pe_raw[b, j])]
+ *   rounded to bf16 (kv_format MLA_KV_BF16: kv_cache bf16 [num_pages,
+ *   page_size, 576]) or quantized per token (MLA_KV_FP8: kv_cache uint8
+ *   codes, kv_scales uint8 [num_pages, page_size]; exponent f = smallest with
+ *   max|row| * 2^-f <= 448, codes = nearest-even E4M3 of row * 2^-f).
+ *  q_nope128     device bf16 [B, q_len, H, 128] (16-byte aligned)
+ *  q_pe_raw      device bf16 [B, q_len, H, 64], before RoPE
+ *  w_uk_t        device bf16 [H, 512, 128]: element [h, c, d] = W_UK[h][d][c]
+ *                (the key up-projection, stored transposed for the absorption)
+ *  c_kv_raw      device bf16 [B, q_len, 512], before the RMSNorm
+ *  kv_norm_w     device bf16 [512]; rms_eps >= 0: RMSNorm(x) = x / sqrt(mean(x^2) + eps)
+ *  k_pe_raw      device bf16 [B, q_len, 64], before RoPE
+ *  rope_cos_sin  device fp32 [max_pos, 64]: row p holds cos of the 32 pair
+ *                angles at position p, then their sin; RoPE turns the pair
+ *                (x[2i], x[2i+1]) by angle i (the table carries any frequency
+ *                scaling).  A position >= max_pos gives NaN in q_pe and no
+ *                cache write.
+ *  seq_lens, block_table, bt_stride, num_pages, page_size: as for
+ *                mla_decode (lengths include the new tokens); a token whose
+ *                page id is outside [0, num_pages) is not written.
+ *  q_nope_absorbed, q_pe: device bf16 outputs [B, q_len, H, 512] / [.., 64].
+ * Two kernels, no allocation, no synchronization.  Errors:
+ * MLA_ERR_INVALID_ARGUMENT, MLA_ERR_HIP.
+ *
+ * mla_up_project -- o[b, j, h] = W_UV[h] attn_out[b, j, h] (bf16, 128 per
+ *   head; the output projection's input).  attn_out: device fp32
+ *   [B, q_len, H, 512] (mla_decode's out), 16-byte aligned; w_uv: device bf16
+ *   [H, 128, 512], 16-byte aligned; o: device bf16 [B, q_len, H, 128].
+ */
+enum { MLA_KV_BF16 = 0, MLA_KV_FP8 = 1 };
+mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads,
+                      const void* q_nope128, const void* q_pe_raw, const void* w_uk_t,
+                      const void* c_kv_raw, const void* kv_norm_w, float rms_eps,
+                      const void* k_pe_raw, const float* rope_cos_sin, int32_t max_pos,
+                      const int32_t* seq_lens, const int32_t* block_table, int32_t bt_stride,
+                      int64_t num_pages, int32_t page_size, int32_t kv_format,
+                      void* kv_cache, void* kv_scales,
+                      void* q_nope_absorbed, void* q_pe, void* stream);
+mla_status mla_up_project(int32_t batch, int32_t q_len, int32_t num_heads,
+                          const float* attn_out, const void* w_uv, void* o, void* stream);
+
 /* Free a plan (its host memory and its device schedule).  NULL is a no-op.
  * The plan must not be in use by a kernel still running. */
 void mla_decode_plan_destroy(mla_plan* plan);

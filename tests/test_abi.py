@@ -213,3 +213,56 @@ def test_fp8_plan_covers_every_key_once():
         assert all(pieces[i][1] == pieces[i + 1][0] for i in range(len(pieces) - 1))
         assert all(lo % 64 == 0 for lo, _ in pieces)  # pieces start on 64-key tiles
     p.destroy()
+
+
+# ---- the prolog / epilog entry points -------------------------------------------------------
+
+
+def _prolog(**over):
+    f = _Fake()
+    a = dict(
+        B=2, q=1, H=128, qn=f(), qpr=f(), wuk=f(), ckv=f(), nw=f(), eps=1e-6, kpe=f(), cs=f(), max_pos=4096,
+        lens=f(), bt=f(), bt_stride=64, num_pages=100, page=64, fmt=bnd.MLA_KV_BF16, cache=f(), scales=None,
+        qa=f(), qp=f(), stream=None,
+    )
+    a.update(over)
+    return mla.lib().mla_prolog(
+        a["B"], a["q"], a["H"], a["qn"], a["qpr"], a["wuk"], a["ckv"], a["nw"], a["eps"], a["kpe"], a["cs"],
+        a["max_pos"], a["lens"], a["bt"], a["bt_stride"], a["num_pages"], a["page"], a["fmt"], a["cache"],
+        a["scales"], a["qa"], a["qp"], a["stream"],
+    )
+
+
+def test_prolog_rejects_null_pointers():
+    for k in ("qn", "qpr", "wuk", "ckv", "nw", "kpe", "cs", "lens", "bt", "cache", "qa", "qp"):
+        assert _prolog(**{k: None}) == 1, k
+    assert _prolog(fmt=bnd.MLA_KV_FP8, scales=None) == 1
+    assert "kv_scales" in mla.lib().mla_last_error().decode()
+
+
+def test_prolog_rejects_bad_sizes_and_formats():
+    for over in (dict(B=0), dict(q=0), dict(q=9), dict(H=0), dict(H=129), dict(page=8), dict(page=48),
+                 dict(page=8192), dict(max_pos=0), dict(bt_stride=0), dict(num_pages=0), dict(fmt=2),
+                 dict(eps=-1.0), dict(eps=float("nan"))):
+        assert _prolog(**over) == 1, over
+
+
+def test_prolog_rejects_misalignment():
+    for k in ("qn", "wuk", "qa", "cache"):
+        assert _prolog(**{k: (1 << 40) + 8}) == 1, k
+    for k in ("qpr", "ckv", "nw", "kpe", "qp", "cs", "lens", "bt"):
+        assert _prolog(**{k: (1 << 40) + 2}) == 1, k
+
+
+def test_up_project_argument_checks():
+    f = _Fake()
+    up = mla.lib().mla_up_project
+    assert up(1, 1, 128, None, f(), f(), None) == 1
+    assert up(1, 1, 128, f(), None, f(), None) == 1
+    assert up(1, 1, 128, f(), f(), None, None) == 1
+    assert up(0, 1, 128, f(), f(), f(), None) == 1
+    assert up(1, 9, 128, f(), f(), f(), None) == 1
+    assert up(1, 1, 129, f(), f(), f(), None) == 1
+    assert up(1, 1, 128, (1 << 40) + 8, f(), f(), None) == 1
+    assert up(1, 1, 128, f(), (1 << 40) + 8, f(), None) == 1
+    assert up(1, 1, 128, f(), f(), (1 << 40) + 4, None) == 1
