@@ -17,6 +17,13 @@ With --kv fp8 the same workload runs over an FP8 cache (E4M3 codes with
 per-token E8M0 scales; seeded codes of the same N(0, 1) draw) on the FP8
 kernel, against the FP8 matrix peak.
 
+With --layer a step is the whole attention of one decode layer around the
+cache: the prolog (absorbed-query projection, RoPE, RMSNorm and the new rows
+appended to the cache), the decode, the combine and the value up-projection;
+value stays the attention's algorithmic TFLOP/s, now over the longer step, and
+the prolog and up-projection report their own HBM rooflines (their weights
+rotate over copies larger than the last-level cache, as each layer has its own).
+
 HBM traffic evidence (roofline.traffic): rocprofv3 counter passes over this
 script, one counter per pass, for the decode workload and for a plain device
 copy of known size (--calibrate-copy), turned into profiles/traffic_<config>.json
@@ -335,6 +342,130 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
     return res
 
 
+def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
+    """The prolog + decode + combine + up-projection step (see the module notes)."""
+    import torch
+
+    import decode_attention_absorbed_amd as mla
+    from decode_attention_absorbed_amd import accounting as acc
+    from decode_attention_absorbed_amd import binding as bnd
+    from workloads import CONFIGS, make_config, make_config_fp8, make_prolog_inputs
+
+    dev = torch.device("cuda:0")
+    fp8 = kv == "fp8"
+    x = make_config_fp8(config) if fp8 else make_config(config)
+    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=CONFIGS[config]["seed"] + 100)
+    lens = [int(v) for v in x.seq_lens]
+    roof = acc.roofline_seconds(lens, x.heads, x.q_len, x.page, kv)
+    B, H, q = x.batch, x.heads, x.q_len
+    M = B * q
+
+    def bf16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    t = x.to_torch(dev)
+    cache_t = t["cache_codes"] if fp8 else t["cache"]
+    copies = max(1, min(16, -(-(1 << 30) // (cache_t.numel() * cache_t.element_size()))))
+    caches = [cache_t] + [cache_t.clone() for _ in range(copies - 1)]
+    scales = ([t["cache_exps"]] + [t["cache_exps"].clone() for _ in range(copies - 1)]) if fp8 else None
+    wcopies = 16  # 16 x 16.8 MB per weight: past the 256 MB last-level cache
+    wuk = [bf16(pi.w_uk_t)] + [None] * (wcopies - 1)
+    wuv = [bf16(pi.w_uv)] + [None] * (wcopies - 1)
+    for i in range(1, wcopies):
+        wuk[i], wuv[i] = wuk[0].clone(), wuv[0].clone()
+    qn128, qpr, ckv, nw, kpe = (bf16(a) for a in (pi.q_nope128, pi.q_pe_raw, pi.c_kv_raw, pi.kv_norm_w, pi.k_pe_raw))
+    table = torch.from_numpy(pi.rope_cos_sin).to(dev)
+    bt, sl = t["block_table"], t["seq_lens"]
+    plan = (bnd.mla_decode_fp8_plan if fp8 else mla.mla_decode_plan)(x.seq_lens, q, H, x.page)
+    q_abs = torch.empty((B, q, H, 512), dtype=torch.bfloat16, device=dev)
+    q_pe = torch.empty((B, q, H, 64), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, q, H), dtype=torch.float32, device=dev)
+    o = torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    L = mla.lib()
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+
+    def prolog(i):
+        c = i % copies
+        bnd._check(L.mla_prolog(B, q, H, qn128.data_ptr(), qpr.data_ptr(), wuk[i % wcopies].data_ptr(), ckv.data_ptr(),
+                                nw.data_ptr(), pi.rms_eps, kpe.data_ptr(), table.data_ptr(), int(table.shape[0]),
+                                sl.data_ptr(), bt.data_ptr(), int(bt.shape[1]), int(caches[c].shape[0]), x.page,
+                                bnd.MLA_KV_FP8 if fp8 else bnd.MLA_KV_BF16, caches[c].data_ptr(),
+                                scales[c].data_ptr() if fp8 else None, q_abs.data_ptr(), q_pe.data_ptr(), s))
+
+    def attend(i):
+        c = i % copies
+        tail = (bt.data_ptr(), int(bt.shape[1]), sl.data_ptr(), float(x.softmax_scale), out.data_ptr(),
+                lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, s)
+        if fp8:
+            bnd._check(L.mla_decode_fp8(plan.handle, q_abs.data_ptr(), q_pe.data_ptr(), caches[c].data_ptr(),
+                                        scales[c].data_ptr(), int(caches[c].shape[0]), *tail))
+        else:
+            bnd._check(L.mla_decode(plan.handle, q_abs.data_ptr(), q_pe.data_ptr(), caches[c].data_ptr(),
+                                    int(caches[c].shape[0]), *tail))
+
+    def up(i):
+        bnd._check(L.mla_up_project(B, q, H, out.data_ptr(), wuv[i % wcopies].data_ptr(), o.data_ptr(), s))
+
+    for i in range(warmup):
+        prolog(i)
+        attend(i)
+        up(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        prolog(i)
+        attend(i)
+        up(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    def burst(fn):
+        n = max(steps, 20)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for i in range(n):
+            fn(i)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / n
+
+    pro_ms, att_ms, up_ms = burst(prolog), burst(attend), burst(up)
+
+    def hbm(nbytes, ms):
+        a = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": acc.PEAK_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+                "frac": a / (acc.PEAK_HBM_BYTES_PER_S / 1e9), "bytes": nbytes, "duration_ms": ms}
+
+    return {
+        "metric": METRIC,
+        "value": roof["flops"] / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations, N(0, 1/fan-in) bf16 weights, random page permutation)",
+        "config": {"workload": f"{config}{'-fp8' if fp8 else ''}-layer", "kv_dtype": kv, "batch": B, "heads": H,
+                   "q_len": q, "page": x.page, "kv_tokens": int(sum(lens)),
+                   "steps_in_step": "prolog + decode + combine + up-projection"},
+        "prolog_ms": pro_ms,
+        "attention_ms": att_ms,
+        "up_project_ms": up_ms,
+        "prolog_roofline": hbm(acc.prolog_bytes(M, H, kv), pro_ms),
+        "up_project_roofline": hbm(acc.up_project_bytes(M, H), up_ms),
+        "attention_share": att_ms / (pro_ms + att_ms + up_ms),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +474,7 @@ def main() -> int:
     ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long | mtp4 | mtp8")
     ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
+    ap.add_argument("--layer", action="store_true", help="time prolog + decode + combine + up-projection per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true", help="run the plain copy the traffic counters are scaled by")
@@ -357,6 +489,9 @@ def main() -> int:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by request; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.layer:
+        print(json.dumps(run_layer(args.config, args.steps, args.warmup, args.kv)), flush=True)
+        return 0
     if args.all:
         for name in ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"]:
             r = run(name, args.steps, args.warmup, False, 0.0, args.kv)

@@ -62,3 +62,27 @@ def roofline_seconds(seq_lens: Sequence[int], heads: int, q_len: int, page: int,
         "bound": "hbm" if t_hbm >= t_mfma else "mfma",
         "t_bound": max(t_hbm, t_mfma),
     }
+
+
+# ---- the steps next to the decode: compulsory bytes (each is bound by HBM) ------------------
+
+D_NOPE, D_ROPE = 128, 64  # per-head query part before the absorption, and the RoPE part
+
+
+def prolog_bytes(rows: int, heads: int, kv: str = "bf16") -> int:
+    """Absorbed-query projection + RoPE + cache append for `rows` = B * q_len
+    new tokens: W_UK (H x 128 x 512 bf16), q_nope in (128 bf16) and the
+    absorbed query out (512 bf16) per row and head, q_pe in and out (64 bf16
+    each), c_kv (512 bf16) and k_pe (64 bf16) in and the cache row out per
+    token, the norm weight and one RoPE table row (64 fp32) per token."""
+    w = heads * D_NOPE * D_V * 2
+    per_head = rows * heads * (D_NOPE * 2 + D_V * 2 + 2 * D_ROPE * 2)
+    row_out = ROW_BYTES_FP8 if kv == "fp8" else ROW_BYTES
+    per_token = rows * ((D_V + D_ROPE) * 2 + row_out + 64 * 4 + 4 + 4)
+    return w + per_head + per_token + D_V * 2
+
+
+def up_project_bytes(rows: int, heads: int) -> int:
+    """Value up-projection: W_UV (H x 128 x 512 bf16), the fp32 attention output
+    in (512 per row and head) and the bf16 result out (128)."""
+    return heads * D_NOPE * D_V * 2 + rows * heads * (D_V * 4 + D_NOPE * 2)

@@ -1262,31 +1262,30 @@ mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads, const voi
   if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8)
     return fail(MLA_ERR_INVALID_ARGUMENT, "kv_format must be MLA_KV_BF16 or MLA_KV_FP8");
   if (kv_format == MLA_KV_FP8 && !kv_scales) return fail(MLA_ERR_INVALID_ARGUMENT, "kv_scales is NULL");
-  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "batch >= 1, q_len in [1, 8] and num_heads in [1, 128] are required");
+  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128 || (int64_t)batch * q_len > (1 << 21))
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "batch >= 1, q_len in [1, 8], batch * q_len <= 2^21 and num_heads in [1, 128] are required");
   if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 4096]");
   if (max_pos < 1 || bt_stride < 1 || num_pages <= 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "max_pos, bt_stride and num_pages must be >= 1");
   if (!std::isfinite(rms_eps) || rms_eps < 0.f) return fail(MLA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
   if (!aligned(q_nope128, 16) || !aligned(w_uk_t, 16) || !aligned(q_nope_absorbed, 16) || !aligned(kv_cache, 16) ||
-      !aligned(q_pe_raw, 4) || !aligned(c_kv_raw, 4) || !aligned(kv_norm_w, 4) || !aligned(k_pe_raw, 4) ||
-      !aligned(q_pe, 4) || !aligned(rope_cos_sin, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4))
+      !aligned(q_pe_raw, 16) || !aligned(q_pe, 16) || !aligned(rope_cos_sin, 16) || !aligned(c_kv_raw, 4) ||
+      !aligned(kv_norm_w, 4) || !aligned(k_pe_raw, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4))
     return fail(MLA_ERR_INVALID_ARGUMENT,
-                "q_nope128, w_uk_t, q_nope_absorbed and kv_cache must be 16-byte aligned, the rest 4-byte aligned");
+                "q_nope128, q_pe_raw, w_uk_t, rope_cos_sin, kv_cache, q_nope_absorbed and q_pe must be 16-byte "
+                "aligned, the rest 4-byte aligned");
   int page_log2 = 0;
   while ((1 << page_log2) < page_size) ++page_log2;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t M = batch * q_len;
-  hipError_t e = mla::launch_absorb(M, num_heads, static_cast<const uint16_t*>(q_nope128),
-                                    static_cast<const uint16_t*>(w_uk_t), static_cast<uint16_t*>(q_nope_absorbed), st);
-  if (e != hipSuccess) return hip_fail(e, "absorption kernel launch");
-  e = mla::launch_rope_append(batch, q_len, num_heads, static_cast<const uint16_t*>(q_pe_raw),
-                              static_cast<const uint16_t*>(c_kv_raw), static_cast<const uint16_t*>(kv_norm_w), rms_eps,
-                              static_cast<const uint16_t*>(k_pe_raw), rope_cos_sin, max_pos, seq_lens, block_table,
-                              bt_stride, num_pages, page_log2, kv_format == MLA_KV_FP8, kv_cache,
-                              static_cast<uint8_t*>(kv_scales), static_cast<uint16_t*>(q_pe), st);
-  if (e != hipSuccess) return hip_fail(e, "rope/append kernel launch");
+  hipError_t e = mla::launch_prolog(
+      batch, q_len, num_heads, static_cast<const uint16_t*>(q_nope128), static_cast<const uint16_t*>(w_uk_t),
+      static_cast<uint16_t*>(q_nope_absorbed), static_cast<const uint16_t*>(q_pe_raw),
+      static_cast<const uint16_t*>(c_kv_raw), static_cast<const uint16_t*>(kv_norm_w), rms_eps,
+      static_cast<const uint16_t*>(k_pe_raw), rope_cos_sin, max_pos, seq_lens, block_table, bt_stride, num_pages,
+      page_log2, kv_format == MLA_KV_FP8, kv_cache, static_cast<uint8_t*>(kv_scales), static_cast<uint16_t*>(q_pe), st);
+  if (e != hipSuccess) return hip_fail(e, "prolog kernel launch");
   g_last_error.clear();
   return MLA_OK;
 }
@@ -1294,8 +1293,9 @@ mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads, const voi
 mla_status mla_up_project(int32_t batch, int32_t q_len, int32_t num_heads, const float* attn_out, const void* w_uv,
                           void* o, void* stream) {
   if (!attn_out || !w_uv || !o) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
-  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "batch >= 1, q_len in [1, 8] and num_heads in [1, 128] are required");
+  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128 || (int64_t)batch * q_len > (1 << 21))
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "batch >= 1, q_len in [1, 8], batch * q_len <= 2^21 and num_heads in [1, 128] are required");
   if (!aligned(attn_out, 16) || !aligned(w_uv, 16) || !aligned(o, 8))
     return fail(MLA_ERR_INVALID_ARGUMENT, "attn_out and w_uv must be 16-byte aligned, o 8-byte aligned");
   hipError_t e = mla::launch_up_project(batch * q_len, num_heads, attn_out, static_cast<const uint16_t*>(w_uv),

@@ -7,17 +7,18 @@
 // and fuses the decode prolog into one operator; the CloudMatrix384 digest
 // (its MLA optimization paragraph) names RMSNorm, the projections and RoPE as
 // its parts.  Here:
-//  * head_gemm_kernel: Y[m, h, :] = W[h] X[m, h, :] per head (W[h] is N x K,
-//    rows contiguous in K).  Absorption: X = q_nope (128), W = W_UK^T
-//    (512 x 128), Y = q_nope_absorbed (bf16).  Up-projection: X = the
-//    attention output (fp32, 512), W = W_UV (128 x 512), Y = o (bf16).
-//    Computed as Y^T = W X^T on v_mfma_f32_16x16x32_bf16 so that a lane's
-//    four results are four consecutive outputs of one row; the weights stream
-//    from HBM once (the operation is bound by their bytes).
-//  * rope_append_kernel: one workgroup per new token: RoPE of every head's
-//    q_pe, RMSNorm of c_kv, RoPE of k_pe, and the row [c_kv | k_pe] (bf16)
-//    written into the paged cache at the token's position, or quantized to
-//    E4M3 with the row's E8M0 exponent for the FP8 cache.
+//  * proj_kernel: Y[m, h, :] = W[h] X[m, h, :] per head (W[h] is N x K, rows
+//    contiguous in K), bound by the weights' bytes.  Absorption: X = q_nope
+//    (128), W = W_UK^T (512 x 128), Y = q_nope_absorbed (bf16).
+//    Up-projection: X = the attention output (fp32, 512), W = W_UV
+//    (128 x 512), Y = o (bf16).
+//  * the prolog is one launch: besides the absorption's workgroups, one more
+//    workgroup per head and chunk of query rows does the per-token part --
+//    RoPE of that head's q_pe, and for the chunk's tokens h, h + H, ... the
+//    RMSNorm of c_kv, RoPE of k_pe and the row [c_kv | k_pe] written into the
+//    paged cache at the token's position (bf16, or E4M3 codes with the row's
+//    E8M0 exponent for the FP8 cache).  These workgroups load no weights, so
+//    their short dependent loads run beside the weight stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,74 +38,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <typename XT>
-__device__ __forceinline__ bf16x8 load_row8(const XT* p);
+// Arguments of the prolog's per-token part (RoPE, RMSNorm, cache append).
+struct PrologArgs {
+  int32_t q_len;
+  const uint16_t* q_pe_raw;
+  const uint16_t* c_kv_raw;
+  const uint16_t* norm_w;
+  float eps;
+  const uint16_t* k_pe_raw;
+  const float* cos_sin;
+  int32_t max_pos;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int64_t num_pages;
+  int32_t page_log2;
+  void* cache;
+  uint8_t* scales;
+  uint16_t* q_pe_out;
+};
 
-template <>
-__device__ __forceinline__ bf16x8 load_row8<uint16_t>(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-template <>
-__device__ __forceinline__ bf16x8 load_row8<float>(const float* p) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
-}
-
-// Workgroup: 4 waves; wave w covers outputs n in [nb + 16 NA w, +16 NA) of
-// head blockIdx.y for rows m in [32 blockIdx.z, +32).  Lane l reads weight row
-// n = nb + 16a + l%16 and input row m = mb + 16b + l%16, K slice 8(l/16) .. +7
-// of each 32-wide K step, and holds outputs n = nb + 16a + 4(l/16) + 0..3 of
-// row m = mb + 16b + l%16.
-template <typename XT, int K, int N, int NA>
-__global__ __launch_bounds__(256) void head_gemm_kernel(int32_t M, int32_t H, const XT* __restrict__ X,
-                                                        const uint16_t* __restrict__ W, uint16_t* __restrict__ Y) {
-  static_assert(K % 32 == 0 && N % (64 * NA) == 0, "tile sizes");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.y;
-  const int nb = blockIdx.x * (64 * NA) + wave * (16 * NA);
-  const int mb = blockIdx.z * 32;
-  const uint16_t* wrow[NA];
-#pragma unroll
-  for (int a = 0; a < NA; ++a) wrow[a] = W + ((size_t)h * N + nb + 16 * a + l16) * K + 8 * grp;
-  const XT* xrow[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int m = min(mb + 16 * b + l16, M - 1);  // rows past M load row M-1 and are not stored
-    xrow[b] = X + ((size_t)m * H + h) * K + 8 * grp;
-  }
-  f32x4 acc[NA][2];
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    bf16x8 wa[NA], xb[2];
-#pragma unroll
-    for (int a = 0; a < NA; ++a) wa[a] = *reinterpret_cast<const bf16x8*>(wrow[a] + k0);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) xb[b] = load_row8<XT>(xrow[b] + k0);
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[a], xb[b], acc[a][b], 0, 0, 0);
-  }
-  typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int m = mb + 16 * b + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      const u16x4 v = {f32_to_bf16(acc[a][b][0]), f32_to_bf16(acc[a][b][1]), f32_to_bf16(acc[a][b][2]),
-                       f32_to_bf16(acc[a][b][3])};
-      *reinterpret_cast<u16x4*>(Y + ((size_t)m * H + h) * N + nb + 16 * a + 4 * grp) = v;
-    }
-  }
+// Position of query row m (= b * q_len + j): L_b - q_len + j.
+__device__ __forceinline__ int row_position(const PrologArgs& a, int m) {
+  const int b = m / a.q_len;
+  return a.seq_lens[b] - a.q_len + (m - b * a.q_len);
 }
 
 // Sum / max over the 256 threads of the workgroup (every thread gets it).
@@ -123,53 +80,60 @@ __device__ __forceinline__ float block_max(float x, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// One workgroup (256 threads) per new token: blockIdx.x = b * q_len + j.
-template <bool FP8>
-__global__ __launch_bounds__(256) void rope_append_kernel(
-    int32_t q_len, int32_t H, const uint16_t* __restrict__ q_pe_raw, const uint16_t* __restrict__ c_kv_raw,
-    const uint16_t* __restrict__ norm_w, float eps, const uint16_t* __restrict__ k_pe_raw,
-    const float* __restrict__ cos_sin, int32_t max_pos, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ block_table, int32_t bt_stride, int64_t num_pages, int32_t page_log2,
-    void* __restrict__ cache, uint8_t* __restrict__ scales, uint16_t* __restrict__ q_pe_out) {
-  __shared__ uint16_t row[576];
-  __shared__ float red[4];
-  const int tok = blockIdx.x;
-  const int b = tok / q_len, j = tok - b * q_len;
-  const int t = threadIdx.x;
-  const int p = seq_lens[b] - q_len + j;  // position of this token
-  const bool valid = p >= 0 && p < max_pos;
-  const float* cs = cos_sin + (size_t)(valid ? p : 0) * 64;
-
-  // q_pe of every head: pair i of head hh turns by the angle of pair i.
-  for (int idx = t; idx < H * 32; idx += 256) {
-    const int hh = idx >> 5, i = idx & 31;
-    const size_t o = ((size_t)tok * H + hh) * 64 + 2 * i;
-    const float x0 = bf16_to_f32(q_pe_raw[o]), x1 = bf16_to_f32(q_pe_raw[o + 1]);
-    const float c = cs[i], s = cs[32 + i];
-    float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
-    if (!valid) y0 = y1 = NAN;  // a position outside the table is loud
-    q_pe_out[o] = f32_to_bf16(y0);
-    q_pe_out[o + 1] = f32_to_bf16(y1);
+// RoPE of q_pe for head h, query rows [m0, m0 + rows): pair i turns by the
+// angle of pair i at the row's position; 4 pairs (16 bytes) per thread step.
+__device__ void rope_query(const PrologArgs& a, int H, int h, int m0, int rows) {
+  for (int v = threadIdx.x; v < rows * 8; v += 256) {
+    const int m = m0 + (v >> 3), c = v & 7;
+    const int p = row_position(a, m);
+    const bool valid = p >= 0 && p < a.max_pos;
+    const size_t o = ((size_t)m * H + h) * 64 + 8 * c;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(a.q_pe_raw + o);
+    const float* cs = a.cos_sin + (size_t)(valid ? p : 0) * 64;
+    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + 4 * c);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(cs + 32 + 4 * c);
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = (float)x[2 * i], x1 = (float)x[2 * i + 1];
+      float y0 = x0 * cv[i] - x1 * sv[i], y1 = x0 * sv[i] + x1 * cv[i];
+      if (!valid) y0 = y1 = NAN;  // a position outside the table is loud
+      y[2 * i] = (__bf16)y0;
+      y[2 * i + 1] = (__bf16)y1;
+    }
+    *reinterpret_cast<bf16x8*>(a.q_pe_out + o) = y;
   }
+}
+
+// The cache row of new token m: [RMSNorm(c_kv) * w | RoPE(k_pe)] in bf16,
+// written at the token's slot as it is (bf16 cache) or as E4M3 codes of
+// row * 2^-f with the E8M0 byte 127 + f (FP8 cache).  Every thread of the
+// workgroup takes part (block reductions); `row` holds 576 bf16 in LDS.
+template <bool FP8>
+__device__ void append_token(const PrologArgs& a, int m, uint16_t* row, float* red) {
+  const int t = threadIdx.x;
+  const int p = row_position(a, m);
+  const bool valid = p >= 0 && p < a.max_pos;
+  const float* cs = a.cos_sin + (size_t)(valid ? p : 0) * 64;
 
   // c_kv: RMSNorm, then the weight.  The values are first scaled by 2^-e
   // (amax = m 2^e, m in [0.5, 1)) so that the fp32 sum of squares neither
   // overflows nor underflows anywhere in the bf16 range; mean + eps and its
   // reciprocal square root are taken in double, and 2^e r (at most
   // sqrt(2048)) scales the scaled values.
-  const float c0 = bf16_to_f32(c_kv_raw[(size_t)tok * 512 + 2 * t]);
-  const float c1 = bf16_to_f32(c_kv_raw[(size_t)tok * 512 + 2 * t + 1]);
+  const float c0 = bf16_to_f32(a.c_kv_raw[(size_t)m * 512 + 2 * t]);
+  const float c1 = bf16_to_f32(a.c_kv_raw[(size_t)m * 512 + 2 * t + 1]);
   const float am = block_max(fmaxf(fabsf(c0), fabsf(c1)), red);
   const int e = am > 0.f ? __builtin_amdgcn_frexp_expf(am) : 0;
   const float a0 = __builtin_ldexpf(c0, -e), a1 = __builtin_ldexpf(c1, -e);
   const float ss = block_sum(a0 * a0 + a1 * a1, red);
-  const double r = 1.0 / __builtin_sqrt(__builtin_ldexp((double)ss * (1.0 / 512.0), 2 * e) + (double)eps);
+  const double r = 1.0 / __builtin_sqrt(__builtin_ldexp((double)ss * (1.0 / 512.0), 2 * e) + (double)a.eps);
   const float rs = (float)__builtin_ldexp(r, e);
-  row[2 * t] = f32_to_bf16(a0 * rs * bf16_to_f32(norm_w[2 * t]));
-  row[2 * t + 1] = f32_to_bf16(a1 * rs * bf16_to_f32(norm_w[2 * t + 1]));
+  row[2 * t] = f32_to_bf16(a0 * rs * bf16_to_f32(a.norm_w[2 * t]));
+  row[2 * t + 1] = f32_to_bf16(a1 * rs * bf16_to_f32(a.norm_w[2 * t + 1]));
   if (t < 32) {
-    const float x0 = bf16_to_f32(k_pe_raw[(size_t)tok * 64 + 2 * t]);
-    const float x1 = bf16_to_f32(k_pe_raw[(size_t)tok * 64 + 2 * t + 1]);
+    const float x0 = bf16_to_f32(a.k_pe_raw[(size_t)m * 64 + 2 * t]);
+    const float x1 = bf16_to_f32(a.k_pe_raw[(size_t)m * 64 + 2 * t + 1]);
     const float c = cs[t], s = cs[32 + t];
     row[512 + 2 * t] = f32_to_bf16(x0 * c - x1 * s);
     row[513 + 2 * t] = f32_to_bf16(x0 * s + x1 * c);
@@ -178,73 +142,184 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
 
   // The slot of the token (an id outside [0, num_pages) or a position outside
   // the table writes nothing).
-  const bool in_table = valid && (p >> page_log2) < bt_stride;
-  const int page = in_table ? block_table[(int64_t)b * bt_stride + (p >> page_log2)] : -1;
-  const bool ok = in_table && (uint64_t)(int64_t)page < (uint64_t)num_pages;
-  const int64_t slot = ((int64_t)page << page_log2) + (p & ((1 << page_log2) - 1));
+  const int b = m / a.q_len;
+  const bool in_table = valid && (p >> a.page_log2) < a.bt_stride;
+  const int page = in_table ? a.block_table[(int64_t)b * a.bt_stride + (p >> a.page_log2)] : -1;
+  const bool ok = in_table && (uint64_t)(int64_t)page < (uint64_t)a.num_pages;
+  const int64_t slot = ((int64_t)page << a.page_log2) + (p & ((1 << a.page_log2) - 1));
   typedef short i16x2 __attribute__((ext_vector_type(2)));
   if constexpr (!FP8) {
     if (ok)
       for (int i = t; i < 288; i += 256)
-        reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(cache) + slot * 576)[i] =
+        reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.cache) + slot * 576)[i] =
             reinterpret_cast<const uint32_t*>(row)[i];
   } else {
     // amax over the bf16 row (exact), the row's exponent f (smallest with
     // amax * 2^-f <= 448, limited to [-127, 127]), codes of row / 2^f.
-    float am = 0.f;
-    for (int i = t; i < 576; i += 256) am = fmaxf(am, fabsf(bf16_to_f32(row[i])));
-    am = block_max(am, red);
+    float amx = 0.f;
+    for (int i = t; i < 576; i += 256) amx = fmaxf(amx, fabsf(bf16_to_f32(row[i])));
+    amx = block_max(amx, red);
     int f = 0;
-    if (am > 0.f) {
-      const int x = __builtin_amdgcn_frexp_expf(am);
-      const float m = __builtin_amdgcn_frexp_mantf(am);
-      f = min(max(x - 9 + (m > 0.875f ? 1 : 0), -127), 127);
+    if (amx > 0.f) {
+      const int x = __builtin_amdgcn_frexp_expf(amx);
+      const float mt = __builtin_amdgcn_frexp_mantf(amx);
+      f = min(max(x - 9 + (mt > 0.875f ? 1 : 0), -127), 127);
     }
     const float sc = __builtin_ldexpf(1.f, f);
     if (ok) {
-      uint8_t* dst = static_cast<uint8_t*>(cache) + slot * 576;
+      uint8_t* dst = static_cast<uint8_t*>(a.cache) + slot * 576;
       for (int i = t; i < 288; i += 256) {
         const uint32_t w = reinterpret_cast<const uint32_t*>(row)[i];
         i16x2 c = {0, 0};
         c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(c, __builtin_bit_cast(bf16x2, w), sc, false);
         reinterpret_cast<uint16_t*>(dst)[i] = (uint16_t)__builtin_bit_cast(uint32_t, c);
       }
-      if (t == 0) scales[slot] = (uint8_t)(127 + f);
+      if (t == 0) a.scales[slot] = (uint8_t)(127 + f);
+    }
+  }
+  __syncthreads();  // `row` and `red` are reused by the next token
+}
+
+// Per-head weight-streaming projection Y[m, h, :] = W[h] X[m, h, :] for the
+// query rows m in [MC z, MC z + MC) (z = blockIdx.z), computed as
+// Y^T = W X^T on v_mfma_f32_16x16x32_bf16.
+//
+// The weights are the bytes that matter (M is small): every lane issues the
+// loads of all its weight fragments at once -- wave w of workgroup x covers
+// rows n in [64 NA x + 16 NA w, +16 NA), lane l row n0 + 16a + l%16 and K
+// slice 8(l/16) of each 32-wide step -- and keeps them in registers.  The
+// chunk of X (its loads issued before the weights', so waiting for it does
+// not wait for them) goes to LDS as bf16, row stride K + 8, which every wave
+// then reads as the B operand: lane l reads row l%16 of a 16-row block, K
+// slice 8(l/16).  A lane's four results are outputs n0 + 16a + 4(l/16) + 0..3
+// of row m = 16-row block + l%16, stored as 8 bytes.
+//
+// With PROLOG >= 0 the workgroups x = N / (64 NA) do the per-token part of the
+// prolog for the chunk instead: RoPE of head h's q_pe, and the cache rows of
+// tokens m0 + h, m0 + h + H, ... (PROLOG = 1: FP8 cache).
+template <typename XT, int K, int N, int NA, int MC, int PROLOG>
+__global__ __launch_bounds__(256) void proj_kernel(int32_t M, int32_t H, const XT* __restrict__ X,
+                                                   const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+                                                   PrologArgs pa) {
+  constexpr int LDK = K + 8;
+  constexpr int KS = K / 32;
+  constexpr int XN = 16 / (int)sizeof(XT);  // elements per 16-byte load
+  constexpr int VPR = K / XN;  // 16-byte vectors per row of X
+  constexpr int PER = MC * VPR / 256;
+  static_assert(K % 32 == 0 && N % (64 * NA) == 0 && MC % 16 == 0 && (MC * VPR) % 256 == 0, "tile sizes");
+  static_assert(MC * LDK >= 576, "the per-token part reuses the X buffer for one cache row");
+  __shared__ __align__(16) uint16_t xs[MC * LDK];
+  __shared__ float red[4];
+
+  const int t = threadIdx.x;
+  const int h = blockIdx.y, m0 = blockIdx.z * MC;
+  const int rows = min(MC, M - m0);
+  if constexpr (PROLOG >= 0) {
+    if (blockIdx.x == N / (64 * NA)) {
+      rope_query(pa, H, h, m0, rows);
+      for (int m = m0 + h; m < m0 + rows; m += H) append_token<PROLOG == 1>(pa, m, xs, red);
+      return;
+    }
+  }
+  const int lane = t & 63, wave = t >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+
+  // Every load of the workgroup is issued up front, as inline asm with
+  // explicit waits (the compiler would otherwise sink the weight loads below
+  // the staging): the chunk of X first -- rows past the chunk's end load (and
+  // stage) its last row again, so no load is conditional -- then all weight
+  // fragments.  Loads complete in order, so once at most NA * KS are
+  // outstanding X has arrived and can be staged while the weights stream.
+  bf16x8 xr[PER];  // 16 raw bytes each: 8 bf16 or 4 fp32
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int v = t + 256 * i, r = min(v / VPR, rows - 1);
+    xr[i] = load16(X + ((size_t)(m0 + r) * H + h) * K + (v % VPR) * XN);
+  }
+  const int nb = blockIdx.x * (64 * NA) + wave * (16 * NA);
+  bf16x8 w[NA][KS];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const uint16_t* wp = W + ((size_t)h * N + nb + 16 * a + l16) * K + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) w[a][s] = load16(wp + 32 * s);
+  }
+  wait_vmem<NA * KS>();
+  // The compiler sees the asm loads' results as ready at once: tie each one to
+  // a volatile asm placed after the wait, so no use moves above it.
+#pragma unroll
+  for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(xr[i]));
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int v = t + 256 * i;
+    uint16_t* dst = xs + (v / VPR) * LDK + (v % VPR) * XN;
+    if constexpr (XN == 8) {
+      *reinterpret_cast<bf16x8*>(dst) = xr[i];
+    } else {
+      typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+      const f32x4 x = __builtin_bit_cast(f32x4, xr[i]);
+      *reinterpret_cast<u16x4*>(dst) = u16x4{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
+    }
+  }
+  __syncthreads();
+  wait_vmem<0>();
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(w[a][s]));
+
+  typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+  for (int mb = 0; mb < rows; mb += 16) {
+    f32x4 acc[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(xs + (mb + l16) * LDK + 32 * s + 8 * grp);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[a][s], b, acc[a], 0, 0, 0);
+    }
+    const int m = m0 + mb + l16;
+    if (m < M) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        *reinterpret_cast<u16x4*>(Y + ((size_t)m * H + h) * N + nb + 16 * a + 4 * grp) =
+            u16x4{f32_to_bf16(acc[a][0]), f32_to_bf16(acc[a][1]), f32_to_bf16(acc[a][2]), f32_to_bf16(acc[a][3])};
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_absorb(int32_t M, int32_t H, const uint16_t* q_nope, const uint16_t* w_uk_t, uint16_t* q_abs,
+constexpr int kAbsorbRows = 128;  // query rows per workgroup chunk of the absorption
+constexpr int kUpRows = 64;       // ... of the up-projection
+
+hipError_t launch_prolog(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_nope, const uint16_t* w_uk_t,
+                         uint16_t* q_abs, const uint16_t* q_pe_raw, const uint16_t* c_kv_raw, const uint16_t* norm_w,
+                         float eps, const uint16_t* k_pe_raw, const float* cos_sin, int32_t max_pos,
+                         const int32_t* seq_lens, const int32_t* block_table, int32_t bt_stride, int64_t num_pages,
+                         int32_t page_log2, bool fp8, void* cache, uint8_t* scales, uint16_t* q_pe_out,
                          hipStream_t stream) {
+  const int32_t M = B * q_len;
+  const PrologArgs pa{q_len,   q_pe_raw,    c_kv_raw,  norm_w,    eps,       k_pe_raw, cos_sin, max_pos,
+                      seq_lens, block_table, bt_stride, num_pages, page_log2, cache,    scales,  q_pe_out};
   constexpr int NA = 2;
-  hipLaunchKernelGGL((head_gemm_kernel<uint16_t, 128, 512, NA>), dim3(512 / (64 * NA), H, (M + 31) / 32), dim3(256),
-                     0, stream, M, H, q_nope, w_uk_t, q_abs);
+  const dim3 grid(512 / (64 * NA) + 1, H, (M + kAbsorbRows - 1) / kAbsorbRows);
+  if (fp8)
+    hipLaunchKernelGGL((proj_kernel<uint16_t, 128, 512, NA, kAbsorbRows, 1>), grid, dim3(256), 0, stream, M, H,
+                       q_nope, w_uk_t, q_abs, pa);
+  else
+    hipLaunchKernelGGL((proj_kernel<uint16_t, 128, 512, NA, kAbsorbRows, 0>), grid, dim3(256), 0, stream, M, H,
+                       q_nope, w_uk_t, q_abs, pa);
   return hipGetLastError();
 }
 
 hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const uint16_t* w_uv, uint16_t* o,
                              hipStream_t stream) {
   constexpr int NA = 1;
-  hipLaunchKernelGGL((head_gemm_kernel<float, 512, 128, NA>), dim3(128 / (64 * NA), H, (M + 31) / 32), dim3(256), 0,
-                     stream, M, H, attn_out, w_uv, o);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_append(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_pe_raw, const uint16_t* c_kv_raw,
-                              const uint16_t* norm_w, float eps, const uint16_t* k_pe_raw, const float* cos_sin,
-                              int32_t max_pos, const int32_t* seq_lens, const int32_t* block_table, int32_t bt_stride,
-                              int64_t num_pages, int32_t page_log2, bool fp8, void* cache, uint8_t* scales,
-                              uint16_t* q_pe_out, hipStream_t stream) {
-  if (fp8)
-    hipLaunchKernelGGL(rope_append_kernel<true>, dim3(B * q_len), dim3(256), 0, stream, q_len, H, q_pe_raw, c_kv_raw,
-                       norm_w, eps, k_pe_raw, cos_sin, max_pos, seq_lens, block_table, bt_stride, num_pages, page_log2,
-                       cache, scales, q_pe_out);
-  else
-    hipLaunchKernelGGL(rope_append_kernel<false>, dim3(B * q_len), dim3(256), 0, stream, q_len, H, q_pe_raw, c_kv_raw,
-                       norm_w, eps, k_pe_raw, cos_sin, max_pos, seq_lens, block_table, bt_stride, num_pages, page_log2,
-                       cache, scales, q_pe_out);
+  const PrologArgs none{};
+  hipLaunchKernelGGL((proj_kernel<float, 512, 128, NA, kUpRows, -1>), dim3(128 / (64 * NA), H, (M + kUpRows - 1) / kUpRows),
+                     dim3(256), 0, stream, M, H, attn_out, w_uv, o, none);
   return hipGetLastError();
 }
 

@@ -240,13 +240,13 @@ mla_status mla_decode_fp8_partials(const mla_plan* plan,
  *   codes, kv_scales uint8 [num_pages, page_size]; exponent f = smallest with
  *   max|row| * 2^-f <= 448, codes = nearest-even E4M3 of row * 2^-f).
  *  q_nope128     device bf16 [B, q_len, H, 128] (16-byte aligned)
- *  q_pe_raw      device bf16 [B, q_len, H, 64], before RoPE
+ *  q_pe_raw      device bf16 [B, q_len, H, 64], before RoPE (16-byte aligned)
  *  w_uk_t        device bf16 [H, 512, 128]: element [h, c, d] = W_UK[h][d][c]
  *                (the key up-projection, stored transposed for the absorption)
  *  c_kv_raw      device bf16 [B, q_len, 512], before the RMSNorm
  *  kv_norm_w     device bf16 [512]; rms_eps >= 0: RMSNorm(x) = x / sqrt(mean(x^2) + eps)
  *  k_pe_raw      device bf16 [B, q_len, 64], before RoPE
- *  rope_cos_sin  device fp32 [max_pos, 64]: row p holds cos of the 32 pair
+ *  rope_cos_sin  device fp32 [max_pos, 64] (16-byte aligned): row p holds cos of the 32 pair
  *                angles at position p, then their sin; RoPE turns the pair
  *                (x[2i], x[2i+1]) by angle i (the table carries any frequency
  *                scaling).  A position >= max_pos gives NaN in q_pe and no
@@ -254,14 +254,18 @@ mla_status mla_decode_fp8_partials(const mla_plan* plan,
  *  seq_lens, block_table, bt_stride, num_pages, page_size: as for
  *                mla_decode (lengths include the new tokens); a token whose
  *                page id is outside [0, num_pages) is not written.
- *  q_nope_absorbed, q_pe: device bf16 outputs [B, q_len, H, 512] / [.., 64].
- * Two kernels, no allocation, no synchronization.  Errors:
+ *  q_nope_absorbed, q_pe: device bf16 outputs [B, q_len, H, 512] / [.., 64],
+ *                16-byte aligned.  batch * q_len <= 2^21; the other
+ *                pointers 4-byte aligned.
+ * One kernel, no allocation, no synchronization.  Errors:
  * MLA_ERR_INVALID_ARGUMENT, MLA_ERR_HIP.
  *
  * mla_up_project -- o[b, j, h] = W_UV[h] attn_out[b, j, h] (bf16, 128 per
- *   head; the output projection's input).  attn_out: device fp32
+ *   head; the output projection's input; the fp32 input is rounded to bf16
+ *   for the bf16 MFMA).  attn_out: device fp32
  *   [B, q_len, H, 512] (mla_decode's out), 16-byte aligned; w_uv: device bf16
- *   [H, 128, 512], 16-byte aligned; o: device bf16 [B, q_len, H, 128].
+ *   [H, 128, 512], 16-byte aligned; o: device bf16 [B, q_len, H, 128],
+ *   8-byte aligned; batch * q_len <= 2^21.  One kernel.
  */
 enum { MLA_KV_BF16 = 0, MLA_KV_FP8 = 1 };
 mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads,

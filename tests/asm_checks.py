@@ -44,15 +44,16 @@ def _split(line: str):
     return parts[0], [o.strip() for o in parts[1].split(",")]
 
 
-def kernel_bodies(asm: str, prefix: str = DECODE_PREFIX) -> list:
-    """Instruction lines of every function whose symbol starts with prefix."""
+def kernel_bodies(asm: str, prefix: str = DECODE_PREFIX, whole: bool = False) -> list:
+    """Instruction lines of every function whose symbol starts with prefix (up
+    to its first s_endpgm, or with ``whole`` to the end of the function)."""
     lines = asm.split("\n")
     out = []
     for i, l in enumerate(lines):
         if l.startswith(prefix) and l.split(";")[0].rstrip().endswith(":"):
             body = []
             for t in lines[i + 1 :]:
-                if "s_endpgm" in t:
+                if (".Lfunc_end" in t) if whole else ("s_endpgm" in t):
                     break
                 t = t.strip()
                 if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
@@ -166,3 +167,30 @@ def store_data_hazards(body: list, need: int = 1) -> list:
 
 def vmcnt_waits(body: list) -> list:
     return [t for t in body if re.match(r"s_waitcnt\b", t) and "vmcnt" in t]
+
+
+def pending_load_violations(body: list) -> list:
+    """Instructions that touch the destination registers of a vector-memory load
+    still outstanding under an in-order vmcnt model: loads and stores count up,
+    `s_waitcnt vmcnt(N)` retires the oldest until N remain.  Catches the use of
+    an inline-asm load (which the compiler does not wait for) before an
+    explicit wait covers it.  Linear in layout order."""
+    pending = []  # destination registers of outstanding operations, oldest first
+    bad = []
+    for t in body:
+        m = re.match(r"s_waitcnt\b.*vmcnt\((\d+)\)", t)
+        if m:
+            del pending[: max(0, len(pending) - int(m.group(1)))]
+            continue
+        op, ops = _split(t)
+        live = set().union(*pending) if pending else set()
+        if op.startswith(("global_", "buffer_")):
+            is_load = "load" in op and "_lds_" not in op
+            srcs = ops[1:] if is_load else ops
+            if any(_regs(o) & live for o in srcs) or (is_load and ops and _regs(ops[0]) & live):
+                bad.append(t)
+            pending.append(_regs(ops[0]) if is_load and ops else set())
+            continue
+        if any(_regs(o) & live for o in ops):
+            bad.append(t)
+    return bad

@@ -241,14 +241,15 @@ def test_prolog_rejects_null_pointers():
 
 
 def test_prolog_rejects_bad_sizes_and_formats():
-    for over in (dict(B=0), dict(q=0), dict(q=9), dict(H=0), dict(H=129), dict(page=8), dict(page=48),
+    for over in (dict(B=0), dict(q=0), dict(q=9), dict(H=0), dict(H=129), dict(B=(1 << 18) + 1, q=8),
+                 dict(page=8), dict(page=48),
                  dict(page=8192), dict(max_pos=0), dict(bt_stride=0), dict(num_pages=0), dict(fmt=2),
                  dict(eps=-1.0), dict(eps=float("nan"))):
         assert _prolog(**over) == 1, over
 
 
 def test_prolog_rejects_misalignment():
-    for k in ("qn", "wuk", "qa", "cache"):
+    for k in ("qn", "qpr", "wuk", "cs", "qa", "qp", "cache"):
         assert _prolog(**{k: (1 << 40) + 8}) == 1, k
     for k in ("qpr", "ckv", "nw", "kpe", "qp", "cs", "lens", "bt"):
         assert _prolog(**{k: (1 << 40) + 2}) == 1, k
@@ -261,6 +262,7 @@ def test_up_project_argument_checks():
     assert up(1, 1, 128, f(), None, f(), None) == 1
     assert up(1, 1, 128, f(), f(), None, None) == 1
     assert up(0, 1, 128, f(), f(), f(), None) == 1
+    assert up((1 << 18) + 1, 8, 128, f(), f(), f(), None) == 1
     assert up(1, 9, 128, f(), f(), f(), None) == 1
     assert up(1, 1, 129, f(), f(), f(), None) == 1
     assert up(1, 1, 128, (1 << 40) + 8, f(), f(), None) == 1

@@ -113,3 +113,52 @@ def test_fp8_async_query_loads_untouched_until_waited(asm_fp8):
     for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
         assert sum(t.startswith("global_load_dwordx4") for t in body) == 36
         assert asm_checks.async_load_violations(body) == []
+
+
+# ---- the prolog / epilog projections -----------------------------------------------------
+
+PROJ_PREFIX = "_ZN3mla12_GLOBAL__N_111proj_kernel"
+
+
+@pytest.fixture(scope="module")
+def asm_prolog(tmp_path_factory):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc):
+        hipcc = shutil.which("hipcc")
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    from decode_attention_absorbed_amd.build import HIP_FLAGS
+
+    out = str(tmp_path_factory.mktemp("asm") / "mla_prolog.s")
+    flags = [f for f in HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "mla_prolog.hip"), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read()
+
+
+def test_projection_loads_issued_up_front(asm_prolog):
+    """absorption (bf16 cache, FP8 cache): 8 X + 8 weight loads per lane;
+    up-projection: 32 X + 16 weight loads; the first wait leaves the weights
+    in flight, the second drains them before the MFMAs."""
+    bodies = asm_checks.kernel_bodies(asm_prolog, prefix=PROJ_PREFIX, whole=True)
+    assert len(bodies) == 3
+    for body in bodies:
+        n = sum(t.startswith("global_load_dwordx4") and t.split(";")[0].rstrip().endswith("off") for t in body)
+        first = next(i for i, t in enumerate(body) if t.startswith("global_load_dwordx4"))
+        run = 0
+        for t in body[first:]:
+            if not t.startswith("global_load_dwordx4"):
+                if t.startswith(("v_", "s_")) and not t.startswith("s_waitcnt"):
+                    continue
+                break
+            run += 1
+        waits = [int(t.split("vmcnt(")[1].split(")")[0]) for t in body if t.startswith("s_waitcnt") and "vmcnt" in t]
+        assert (run, waits[:2]) in ((16, [8, 0]), (48, [16, 0])), (run, waits[:4], n)
+        assert sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in body) in (8, 16)
+
+
+def test_projection_loads_untouched_until_waited(asm_prolog):
+    for body in asm_checks.kernel_bodies(asm_prolog, prefix=PROJ_PREFIX, whole=True):
+        assert asm_checks.pending_load_violations(body) == []
