@@ -292,7 +292,6 @@ __global__ __launch_bounds__(256) void proj_kernel(int32_t M, int32_t H, const X
 }  // namespace
 
 constexpr int kAbsorbRows = 128;  // query rows per workgroup chunk of the absorption
-constexpr int kUpRows = 64;       // ... of the up-projection
 
 hipError_t launch_prolog(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_nope, const uint16_t* w_uk_t,
                          uint16_t* q_abs, const uint16_t* q_pe_raw, const uint16_t* c_kv_raw, const uint16_t* norm_w,
@@ -316,10 +315,17 @@ hipError_t launch_prolog(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_
 
 hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const uint16_t* w_uv, uint16_t* o,
                              hipStream_t stream) {
-  constexpr int NA = 1;
   const PrologArgs none{};
-  hipLaunchKernelGGL((proj_kernel<float, 512, 128, NA, kUpRows, -1>), dim3(128 / (64 * NA), H, (M + kUpRows - 1) / kUpRows),
-                     dim3(256), 0, stream, M, H, attn_out, w_uv, o, none);
+  if (M <= 64) {
+    // two workgroups per head (64 outputs each), all rows in one chunk
+    hipLaunchKernelGGL((proj_kernel<float, 512, 128, 1, 64, -1>), dim3(2, H, 1), dim3(256), 0, stream, M, H, attn_out,
+                       w_uv, o, none);
+  } else {
+    // one workgroup per head and 32-row chunk: the fp32 input (the larger
+    // operand at these sizes) is read once
+    hipLaunchKernelGGL((proj_kernel<float, 512, 128, 2, 32, -1>), dim3(1, H, (M + 31) / 32), dim3(256), 0, stream, M,
+                       H, attn_out, w_uv, o, none);
+  }
   return hipGetLastError();
 }
 

@@ -248,7 +248,7 @@ def test_prolog_positions_outside_the_table_and_pages(dev):
 
 def test_up_project_small(dev):
     rng = np.random.default_rng(19)
-    for B, q, H in ((1, 1, 1), (37, 1, 16), (5, 4, 128), (3, 8, 3)):
+    for B, q, H in ((1, 1, 1), (37, 1, 16), (5, 4, 128), (3, 8, 3), (9, 8, 16), (100, 1, 4)):  # M = 1 .. 100
         pi = make_prolog_inputs(B, q, H, [q] * B, seed=20)
         a = (rng.standard_normal((B, q, H, 512)) * 0.5).astype(np.float32)
         o = mla.mla_up_project(torch.from_numpy(a).to(dev), bf16_dev(pi.w_uv, dev))
