@@ -24,7 +24,8 @@
 
 #include <cmath>
 
-#include "prolog.h"
+#include "abi_common.h"
+#include "mla_decode.h"
 
 namespace mla {
 namespace {
@@ -330,3 +331,62 @@ hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const 
 }
 
 }  // namespace mla
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+
+mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads, const void* q_nope128, const void* q_pe_raw,
+                      const void* w_uk_t, const void* c_kv_raw, const void* kv_norm_w, float rms_eps,
+                      const void* k_pe_raw, const float* rope_cos_sin, int32_t max_pos, const int32_t* seq_lens,
+                      const int32_t* block_table, int32_t bt_stride, int64_t num_pages, int32_t page_size,
+                      int32_t kv_format, void* kv_cache, void* kv_scales, void* q_nope_absorbed, void* q_pe,
+                      void* stream) {
+  if (!q_nope128 || !q_pe_raw || !w_uk_t || !c_kv_raw || !kv_norm_w || !k_pe_raw || !rope_cos_sin || !seq_lens ||
+      !block_table || !kv_cache || !q_nope_absorbed || !q_pe)
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8)
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "kv_format must be MLA_KV_BF16 or MLA_KV_FP8");
+  if (kv_format == MLA_KV_FP8 && !kv_scales) return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "kv_scales is NULL");
+  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128 || (int64_t)batch * q_len > (1 << 21))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT,
+                "batch >= 1, q_len in [1, 8], batch * q_len <= 2^21 and num_heads in [1, 128] are required");
+  if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 4096]");
+  if (max_pos < 1 || bt_stride < 1 || num_pages <= 0)
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "max_pos, bt_stride and num_pages must be >= 1");
+  if (!std::isfinite(rms_eps) || rms_eps < 0.f) return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  if (!mla::abi_aligned(q_nope128, 16) || !mla::abi_aligned(w_uk_t, 16) || !mla::abi_aligned(q_nope_absorbed, 16) || !mla::abi_aligned(kv_cache, 16) ||
+      !mla::abi_aligned(q_pe_raw, 16) || !mla::abi_aligned(q_pe, 16) || !mla::abi_aligned(rope_cos_sin, 16) || !mla::abi_aligned(c_kv_raw, 4) ||
+      !mla::abi_aligned(kv_norm_w, 4) || !mla::abi_aligned(k_pe_raw, 4) || !mla::abi_aligned(seq_lens, 4) || !mla::abi_aligned(block_table, 4))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT,
+                "q_nope128, q_pe_raw, w_uk_t, rope_cos_sin, kv_cache, q_nope_absorbed and q_pe must be 16-byte "
+                "aligned, the rest 4-byte aligned");
+  int page_log2 = 0;
+  while ((1 << page_log2) < page_size) ++page_log2;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_prolog(
+      batch, q_len, num_heads, static_cast<const uint16_t*>(q_nope128), static_cast<const uint16_t*>(w_uk_t),
+      static_cast<uint16_t*>(q_nope_absorbed), static_cast<const uint16_t*>(q_pe_raw),
+      static_cast<const uint16_t*>(c_kv_raw), static_cast<const uint16_t*>(kv_norm_w), rms_eps,
+      static_cast<const uint16_t*>(k_pe_raw), rope_cos_sin, max_pos, seq_lens, block_table, bt_stride, num_pages,
+      page_log2, kv_format == MLA_KV_FP8, kv_cache, static_cast<uint8_t*>(kv_scales), static_cast<uint16_t*>(q_pe), st);
+  if (e != hipSuccess) return mla::abi_hip_fail(e, "prolog kernel launch");
+  mla::abi_ok();
+  return MLA_OK;
+}
+
+mla_status mla_up_project(int32_t batch, int32_t q_len, int32_t num_heads, const float* attn_out, const void* w_uv,
+                          void* o, void* stream) {
+  if (!attn_out || !w_uv || !o) return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (batch < 1 || q_len < 1 || q_len > 8 || num_heads < 1 || num_heads > 128 || (int64_t)batch * q_len > (1 << 21))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT,
+                "batch >= 1, q_len in [1, 8], batch * q_len <= 2^21 and num_heads in [1, 128] are required");
+  if (!mla::abi_aligned(attn_out, 16) || !mla::abi_aligned(w_uv, 16) || !mla::abi_aligned(o, 8))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "attn_out and w_uv must be 16-byte aligned, o 8-byte aligned");
+  hipError_t e = mla::launch_up_project(batch * q_len, num_heads, attn_out, static_cast<const uint16_t*>(w_uv),
+                                        static_cast<uint16_t*>(o), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return mla::abi_hip_fail(e, "up-projection kernel launch");
+  mla::abi_ok();
+  return MLA_OK;
+}
