@@ -29,7 +29,9 @@ the others in the design notes):
     plain RoPE and frequency-scaled variants are the caller's table);
     RMSNorm is x / sqrt(mean(x^2) + eps) * w;
   * epilog: the value up-projection o_h = W_UV[h] out_h (128 wide per head),
-    the input of the output projection.
+    the input of the output projection; then the output projection itself,
+    y = W_O [o_0 | o_1 | ... | o_{H-1}] (heads concatenated in order, W_O of
+    shape [hidden, H * 128] as a linear layer stores it).
 """
 from __future__ import annotations
 
@@ -134,3 +136,11 @@ def rope_table(theta: float, max_pos: int) -> Tuple[np.ndarray, np.ndarray]:
     inv = theta ** (-np.arange(0, D_ROPE, 2, dtype=np.float64) / D_ROPE)
     ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
     return np.cos(ang), np.sin(ang)
+
+
+def o_project_ref(o: np.ndarray, W_O: np.ndarray) -> np.ndarray:
+    """y[..., :] = W_O @ concat_h o[..., h, :] (o [..., H, 128], W_O [N, H * 128])."""
+    o = np.asarray(o, np.float64)
+    x = o.reshape(o.shape[:-2] + (o.shape[-2] * o.shape[-1],))
+    return x @ np.asarray(W_O, np.float64).T
+

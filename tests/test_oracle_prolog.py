@@ -9,6 +9,7 @@ from oracle.mla_oracle_fp8 import e4m3_decode
 from oracle.mla_prolog_oracle import (
     append_ref,
     bf16_round,
+    o_project_ref,
     positions,
     prolog_ref,
     quantize_row_fp8,
@@ -141,3 +142,31 @@ def test_up_projection_completes_the_unabsorbed_attention():
     np.testing.assert_allclose(lse, lse_ref, rtol=1e-12)
     # and per head it is the plain matrix-vector product
     np.testing.assert_allclose(up_project_ref(out, W_UV)[1, 0, 2], W_UV[2] @ out[1, 0, 2], rtol=1e-12)
+
+
+def test_o_projection_per_head_blocks():
+    """The output projection of the concatenated heads is the sum over heads of
+    each head's 128 columns of W_O applied to that head (brute force), and with
+    the up-projection it completes the ordinary multi-head attention."""
+    rng = np.random.default_rng(9)
+    o = rng.standard_normal((2, 3, 4, 128))
+    W = rng.standard_normal((40, 4 * 128))
+    y = o_project_ref(o, W)
+    assert y.shape == (2, 3, 40)
+    for b, j in ((0, 0), (1, 2)):
+        ref = sum(W[:, h * 128:(h + 1) * 128] @ o[b, j, h] for h in range(4))
+        np.testing.assert_allclose(y[b, j], ref, rtol=1e-12, atol=1e-12)
+        n = 7
+        brute = sum(W[n, h * 128 + d] * o[b, j, h, d] for h in range(4) for d in range(128))
+        assert abs(y[b, j, n] - brute) < 1e-10
+    # the whole chain: absorbed attention, up-projection, output projection =
+    # the unabsorbed multi-head attention's output projected
+    x = make_inputs(2, 3, 1, 8, [11, 25], seed=10)
+    qn128 = rng.standard_normal((2, 1, 3, 128))
+    W_UK = rng.standard_normal((3, 128, 512)) / math.sqrt(512)
+    W_UV = rng.standard_normal((3, 128, 512)) / math.sqrt(512)
+    W_O = rng.standard_normal((24, 3 * 128))
+    o_ref, _ = mha_unabsorbed_ref(qn128, x.q_pe_f64(), x.cache_f64(), x.block_table, x.seq_lens, W_UK, W_UV, SCALE)
+    out, _ = mla_decode_ref(absorb_query(qn128, W_UK), x.q_pe_f64(), x.cache_f64(), x.block_table, x.seq_lens, SCALE)
+    np.testing.assert_allclose(o_project_ref(up_project_ref(out, W_UV), W_O), o_project_ref(o_ref, W_O), rtol=1e-9, atol=1e-11)
+

@@ -415,6 +415,7 @@ class PrologInputs:
     k_pe_raw: np.ndarray  # uint16 [B, q_len, 64]
     rope_cos_sin: np.ndarray  # float32 [max_pos, 64]: cos of the 32 pair angles, then their sin
     w_uv: np.ndarray  # uint16 [H, 128, 512]
+    w_o: Optional[np.ndarray] = None  # uint16 [hidden, H * 128] (drawn when hidden > 0)
     rms_eps: float = 1e-6
 
     def w_uk_f64(self) -> np.ndarray:
@@ -430,10 +431,13 @@ def rope_cos_sin_table(max_pos: int, theta: float = ROPE_THETA) -> np.ndarray:
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
 
 
-def make_prolog_inputs(batch: int, q_len: int, heads: int, seq_lens: Sequence[int], seed: int) -> PrologInputs:
+def make_prolog_inputs(
+    batch: int, q_len: int, heads: int, seq_lens: Sequence[int], seed: int, hidden: int = 0
+) -> PrologInputs:
     """Draw order: q_nope (128 wide), q_pe, W_UK^T, c_kv, the norm weight, k_pe,
-    W_UV; values N(0, 1) except the weights (N(0, 1/sqrt(fan-in))) and the
-    norm weight (1 + 0.1 N(0, 1)); all rounded to bf16."""
+    W_UV, then (hidden > 0) the output projection W_O [hidden, H * 128]; values
+    N(0, 1) except the weights (N(0, 1/sqrt(fan-in))) and the norm weight
+    (1 + 0.1 N(0, 1)); all rounded to bf16.  DeepSeek-V3's hidden size is 7168."""
     rng = np.random.default_rng(seed)
     n = lambda *s: rng.standard_normal(s, dtype=np.float32)
     q_nope = to_bf16_bits(n(batch, q_len, heads, 128))
@@ -443,8 +447,10 @@ def make_prolog_inputs(batch: int, q_len: int, heads: int, seq_lens: Sequence[in
     w = to_bf16_bits(np.float32(1.0) + np.float32(0.1) * n(D_LATENT))
     k_pe = to_bf16_bits(n(batch, q_len, D_ROPE))
     w_uv = to_bf16_bits(n(heads, 128, D_LATENT) / np.float32(np.sqrt(float(D_LATENT))))
+    w_o = to_bf16_bits(n(hidden, heads * 128) / np.float32(np.sqrt(heads * 128.0))) if hidden > 0 else None
     lens = np.asarray(seq_lens, np.int32)
     return PrologInputs(
         batch=batch, q_len=q_len, heads=heads, seq_lens=lens, q_nope128=q_nope, q_pe_raw=q_pe, w_uk_t=w_uk_t,
         c_kv_raw=c_kv, kv_norm_w=w, k_pe_raw=k_pe, rope_cos_sin=rope_cos_sin_table(int(lens.max()) + 1), w_uv=w_uv,
+        w_o=w_o,
     )
