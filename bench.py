@@ -19,7 +19,8 @@ kernel, against the FP8 matrix peak.
 
 With --layer a step is the whole attention of one decode layer around the
 cache: the prolog (absorbed-query projection, RoPE, RMSNorm and the new rows
-appended to the cache), the decode, the combine and the value up-projection;
+appended to the cache), the decode, the combine, the value up-projection and
+the output projection (to DeepSeek-V3's 7168-wide hidden state);
 value stays the attention's algorithmic TFLOP/s, now over the longer step, and
 the prolog and up-projection report their own HBM rooflines (their weights
 rotate over copies larger than the last-level cache, as each layer has its own).
@@ -343,7 +344,7 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
 
 
 def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
-    """The prolog + decode + combine + up-projection step (see the module notes)."""
+    """The prolog + decode + combine + up-projection + output projection step (see the module notes)."""
     import torch
 
     import decode_attention_absorbed_amd as mla
@@ -354,7 +355,8 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
     dev = torch.device("cuda:0")
     fp8 = kv == "fp8"
     x = make_config_fp8(config) if fp8 else make_config(config)
-    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=CONFIGS[config]["seed"] + 100)
+    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=CONFIGS[config]["seed"] + 100,
+                            hidden=acc.HIDDEN)
     lens = [int(v) for v in x.seq_lens]
     roof = acc.roofline_seconds(lens, x.heads, x.q_len, x.page, kv)
     B, H, q = x.batch, x.heads, x.q_len
@@ -373,6 +375,13 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
     wuv = [bf16(pi.w_uv)] + [None] * (wcopies - 1)
     for i in range(1, wcopies):
         wuk[i], wuv[i] = wuk[0].clone(), wuv[0].clone()
+    ocopies = 4  # 4 x 235 MB of W_O
+    wo = [bf16(pi.w_o)]
+    wo += [wo[0].clone() for _ in range(ocopies - 1)]
+    N_o, K_o = int(pi.w_o.shape[0]), int(pi.w_o.shape[1])
+    y = torch.empty((B, q, N_o), dtype=torch.bfloat16, device=dev)
+    ows_bytes = bnd.mla_o_project_workspace_bytes(B, q, K_o, N_o)
+    ows = torch.empty(max(ows_bytes, 16), dtype=torch.uint8, device=dev)
     qn128, qpr, ckv, nw, kpe = (bf16(a) for a in (pi.q_nope128, pi.q_pe_raw, pi.c_kv_raw, pi.kv_norm_w, pi.k_pe_raw))
     table = torch.from_numpy(pi.rope_cos_sin).to(dev)
     bt, sl = t["block_table"], t["seq_lens"]
@@ -409,10 +418,15 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
     def up(i):
         bnd._check(L.mla_up_project(B, q, H, out.data_ptr(), wuv[i % wcopies].data_ptr(), o.data_ptr(), s))
 
+    def oproj(i):
+        bnd._check(L.mla_o_project(B, q, K_o, N_o, o.data_ptr(), wo[i % ocopies].data_ptr(), y.data_ptr(),
+                                   ows.data_ptr(), ows_bytes, s))
+
     for i in range(warmup):
         prolog(i)
         attend(i)
         up(i)
+        oproj(i)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -420,6 +434,7 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
         prolog(i)
         attend(i)
         up(i)
+        oproj(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
@@ -434,7 +449,7 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
         torch.cuda.synchronize()
         return b0.elapsed_time(b1) / n
 
-    pro_ms, att_ms, up_ms = burst(prolog), burst(attend), burst(up)
+    pro_ms, att_ms, up_ms, op_ms = burst(prolog), burst(attend), burst(up), burst(oproj)
 
     def hbm(nbytes, ms):
         a = nbytes / (ms * 1e-3) / 1e9
@@ -456,13 +471,15 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
         "data": "synthetic (seeded N(0,1) bf16 activations, N(0, 1/fan-in) bf16 weights, random page permutation)",
         "config": {"workload": f"{config}{'-fp8' if fp8 else ''}-layer", "kv_dtype": kv, "batch": B, "heads": H,
                    "q_len": q, "page": x.page, "kv_tokens": int(sum(lens)),
-                   "steps_in_step": "prolog + decode + combine + up-projection"},
+                   "hidden": N_o, "steps_in_step": "prolog + decode + combine + up-projection + output projection"},
         "prolog_ms": pro_ms,
         "attention_ms": att_ms,
         "up_project_ms": up_ms,
         "prolog_roofline": hbm(acc.prolog_bytes(M, H, kv), pro_ms),
         "up_project_roofline": hbm(acc.up_project_bytes(M, H), up_ms),
-        "attention_share": att_ms / (pro_ms + att_ms + up_ms),
+        "o_project_ms": op_ms,
+        "o_project_roofline": hbm(acc.o_project_bytes(M, H, N_o), op_ms),
+        "attention_share": att_ms / (pro_ms + att_ms + up_ms + op_ms),
     }
 
 
@@ -474,7 +491,8 @@ def main() -> int:
     ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long | mtp4 | mtp8")
     ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
-    ap.add_argument("--layer", action="store_true", help="time prolog + decode + combine + up-projection per step")
+    ap.add_argument("--layer", action="store_true",
+                    help="time prolog + decode + combine + up-projection + output projection per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true", help="run the plain copy the traffic counters are scaled by")

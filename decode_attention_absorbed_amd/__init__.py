@@ -15,5 +15,7 @@ from .binding import (  # noqa: F401
     mla_decode_plan_host,
     mla_decode_workspace_bytes,
     mla_prolog,
+    mla_o_project,
+    mla_o_project_workspace_bytes,
     mla_up_project,
 )

@@ -86,3 +86,14 @@ def up_project_bytes(rows: int, heads: int) -> int:
     """Value up-projection: W_UV (H x 128 x 512 bf16), the fp32 attention output
     in (512 per row and head) and the bf16 result out (128)."""
     return heads * D_NOPE * D_V * 2 + rows * heads * (D_V * 4 + D_NOPE * 2)
+
+
+HIDDEN = 7168  # DeepSeek-V3's model width: the output projection's rows
+
+
+def o_project_bytes(rows: int, heads: int, hidden: int = HIDDEN) -> int:
+    """Output projection: W_O (hidden x H*128 bf16), its bf16 input (H*128 per
+    row) and bf16 output (hidden per row); the fp32 partial sums over slices
+    of the input width are not compulsory and are not counted."""
+    k = heads * D_NOPE
+    return hidden * k * 2 + rows * (k + hidden) * 2

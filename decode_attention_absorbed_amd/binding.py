@@ -52,6 +52,8 @@ EXPORTED = (
     "mla_decode_fp8_partials",
     "mla_prolog",
     "mla_up_project",
+    "mla_o_project_workspace_bytes",
+    "mla_o_project",
 )
 
 #: kv_format values of mla_prolog
@@ -124,6 +126,10 @@ def lib() -> ctypes.CDLL:
     L.mla_prolog.restype = ctypes.c_int
     L.mla_up_project.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     L.mla_up_project.restype = ctypes.c_int
+    L.mla_o_project_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+    L.mla_o_project_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_o_project.argtypes = [ctypes.c_int32] * 4 + [vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.mla_o_project.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -440,3 +446,43 @@ def mla_up_project(
         stream = torch.cuda.current_stream(attn_out.device)
     _check(lib().mla_up_project(B, qlen, H, _ptr(attn_out), _ptr(w_uv), _ptr(o), stream.cuda_stream))
     return o
+
+
+def mla_o_project_workspace_bytes(batch: int, q_len: int, k_in: int, n_out: int) -> int:
+    return int(lib().mla_o_project_workspace_bytes(batch, q_len, k_in, n_out))
+
+
+def mla_o_project(
+    o: torch.Tensor,
+    w_o: torch.Tensor,
+    y: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> torch.Tensor:
+    """Enqueue y = W_O concat_h(o) for o bf16 [B, q_len, H, 128] (mla_up_project's
+    output) and w_o bf16 [n_out, H * 128]; returns y (bf16 [B, q_len, n_out])."""
+    if o.dim() != 4 or o.shape[3] != 128:
+        raise ValueError(f"o: shape {tuple(o.shape)}, expected [B, q_len, H, 128]")
+    B, qlen, H = (int(v) for v in o.shape[:3])
+    K = H * 128
+    _expect(o, "o", torch.bfloat16, (B, qlen, H, 128))
+    if w_o.dim() != 2 or w_o.shape[1] != K:
+        raise ValueError(f"w_o: shape {tuple(w_o.shape)}, expected [n_out, {K}]")
+    _expect(w_o, "w_o", torch.bfloat16, tuple(w_o.shape))
+    N = int(w_o.shape[0])
+    if y is None:
+        y = torch.empty((B, qlen, N), dtype=torch.bfloat16, device=o.device)
+    _expect(y, "y", torch.bfloat16, (B, qlen, N))
+    need = mla_o_project_workspace_bytes(B, qlen, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=o.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o.device)
+    _check(
+        lib().mla_o_project(
+            B, qlen, K, N, _ptr(o), _ptr(w_o), _ptr(y), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), stream.cuda_stream,
+        )
+    )
+    return y
+

@@ -12,6 +12,9 @@
 //    (128), W = W_UK^T (512 x 128), Y = q_nope_absorbed (bf16).
 //    Up-projection: X = the attention output (fp32, 512), W = W_UV
 //    (128 x 512), Y = o (bf16).
+//  * oproj_kernel + sum_kernel: the output projection Y = X W_O^T (X the
+//    up-projected heads concatenated, [M, K]; W_O [N, K]), split over K into
+//    S slices whose fp32 partials a second launch sums into bf16.
 //  * the prolog is one launch: besides the absorption's workgroups, one more
 //    workgroup per head and chunk of query rows does the per-token part --
 //    RoPE of that head's q_pe, and for the chunk's tokens h, h + H, ... the
@@ -290,6 +293,99 @@ __global__ __launch_bounds__(256) void proj_kernel(int32_t M, int32_t H, const X
   }
 }
 
+
+// Output projection, split over K: slice s = blockIdx.y covers K columns
+// [s * kslice, +kslice); P[s][m][n] (fp32) = sum over the slice of
+// X[m, k] W[n, k].  Wave w of workgroup x owns output rows n in
+// [64 x + 16 w, +16) (lane l: row l%16, K slice 8(l/16) of each 32-wide step)
+// and query rows [MC z, +MC).  The slice is walked in KC-column chunks: the
+// chunk of X (its loads first) and the wave's KC / 32 weight fragments are issued
+// together as asm loads, X is staged in LDS as the MFMA's B operand, and the
+// 16-row blocks of X accumulate in registers.  Several workgroups per CU keep
+// the weight stream going while one of them computes.
+template <int MC, int KC>
+__global__ __launch_bounds__(256) void oproj_kernel(int32_t M, int32_t N, int32_t K, int32_t kslice,
+                                                    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                    float* __restrict__ P) {
+  constexpr int LDK = KC + 8, KS = KC / 32;
+  constexpr int VPR = KC / 8;           // 16-byte vectors per row of a chunk
+  constexpr int PER = MC * VPR / 256;   // ... per thread
+  constexpr int MB = MC / 16;           // 16-row blocks
+  __shared__ __align__(16) uint16_t xs[MC * LDK];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int s = blockIdx.y, m0 = blockIdx.z * MC;
+  const int rows = min(MC, M - m0);
+  f32x4 acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wp = W + (size_t)(n0 + l16) * K + 8 * grp;
+  // Workgroups of neighbouring row blocks walk their slice's chunks from
+  // different starting points: all workgroups run at once, and in lockstep
+  // they would read the same column offset of rows 2K bytes apart, which
+  // lands on few HBM channels (measured: 4.0 vs 6.1 TB/s for a 256 MB read).
+  const int nch = kslice / KC;
+  for (int c = 0; c < nch; ++c) {
+    const int kc = s * kslice + ((c + (int)blockIdx.x) % nch) * KC;
+    bf16x8 xr[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = t + 256 * i, r = min(v / VPR, rows - 1);  // rows past the end repeat the last one
+      xr[i] = load16(X + (size_t)(m0 + r) * K + kc + 8 * (v % VPR));
+    }
+    bf16x8 w[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) w[j] = load16(wp + kc + 32 * j);
+    wait_vmem<KS>();  // X has arrived (loads complete in order); the weights stream on
+#pragma unroll
+    for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(xr[i]));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = t + 256 * i;
+      *reinterpret_cast<bf16x8*>(xs + (v / VPR) * LDK + 8 * (v % VPR)) = xr[i];
+    }
+    __syncthreads();
+    wait_vmem<0>();
+#pragma unroll
+    for (int j = 0; j < KS; ++j) asm volatile("" : "+v"(w[j]));
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      if (16 * b < rows) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(xs + (16 * b + l16) * LDK + 32 * j + 8 * grp);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], x, acc[b], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the next chunk overwrites xs
+  }
+  // lane: outputs n0 + 4(l/16) + 0..3 of row 16b + l%16
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int m = m0 + 16 * b + l16;
+    if (m < M) *reinterpret_cast<f32x4*>(P + ((size_t)s * M + m) * N + n0 + 4 * grp) = acc[b];
+  }
+}
+
+// Y[m, n] (bf16) = sum over the S slices of P[s][m][n]; 4 outputs per thread.
+__global__ __launch_bounds__(256) void sum_kernel(int64_t MN4, int32_t S, int64_t MN, const float* __restrict__ P,
+                                                  uint16_t* __restrict__ Y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN4) return;
+  f32x4 a = *reinterpret_cast<const f32x4*>(P + 4 * i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(P + (size_t)s * MN + 4 * i);
+    a[0] += b[0];
+    a[1] += b[1];
+    a[2] += b[2];
+    a[3] += b[3];
+  }
+  typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<u16x4*>(Y + 4 * i) = u16x4{f32_to_bf16(a[0]), f32_to_bf16(a[1]), f32_to_bf16(a[2]), f32_to_bf16(a[3])};
+}
+
 }  // namespace
 
 constexpr int kAbsorbRows = 128;  // query rows per workgroup chunk of the absorption
@@ -327,6 +423,46 @@ hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const 
     hipLaunchKernelGGL((proj_kernel<float, 512, 128, 2, 32, -1>), dim3(1, H, (M + 31) / 32), dim3(256), 0, stream, M,
                        H, attn_out, w_uv, o, none);
   }
+  return hipGetLastError();
+}
+
+// Split of K for the output projection: rows per chunk 32, 64 or 128 (the
+// smallest that holds every row: X's staging loads scale with it); columns
+// per chunk and slices (S at most, halved until it divides K into whole
+// chunks) from interleaved A/B runs at 7168 x 16384: 128 columns and 4 slices
+// for up to 32 rows, 256 and 8 up to 64, 256 and 4 above.  Narrower chunks
+// spread the concurrently read column offsets over more HBM channels; wider
+// ones (512) or fewer slices (2) were 35-60% slower.
+void oproj_split(int32_t M, int32_t K, int* mc, int* S, int* kc) {
+  *mc = M > 64 ? 128 : M > 32 ? 64 : 32;
+  *kc = *mc == 32 ? 128 : 256;
+  int s = M > 64 || M <= 32 ? 4 : 8;
+  while (s > 1 && (K / *kc) % s != 0) s >>= 1;
+  *S = s;
+}
+
+size_t oproj_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  int mc, S, kc;
+  oproj_split(M, K, &mc, &S, &kc);
+  return (size_t)S * M * N * sizeof(float);
+}
+
+hipError_t launch_o_project(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint16_t* w, uint16_t* y,
+                            float* partials, hipStream_t stream) {
+  int mc, S, kc;
+  oproj_split(M, K, &mc, &S, &kc);
+  const dim3 grid(N / 64, S, (M + mc - 1) / mc);
+  if (mc == 32)
+    hipLaunchKernelGGL((oproj_kernel<32, 128>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  else if (mc == 64)
+    hipLaunchKernelGGL((oproj_kernel<64, 256>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  else
+    hipLaunchKernelGGL((oproj_kernel<128, 256>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t mn4 = (int64_t)M * N / 4;
+  hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((mn4 + 255) / 256)), dim3(256), 0, stream, mn4, S, (int64_t)M * N,
+                     partials, y);
   return hipGetLastError();
 }
 
@@ -390,3 +526,34 @@ mla_status mla_up_project(int32_t batch, int32_t q_len, int32_t num_heads, const
   mla::abi_ok();
   return MLA_OK;
 }
+
+size_t mla_o_project_workspace_bytes(int32_t batch, int32_t q_len, int32_t k_in, int32_t n_out) {
+  if (batch < 1 || q_len < 1 || q_len > 8 || k_in < 256 || k_in % 256 != 0 || k_in > (1 << 20) || n_out < 64 ||
+      n_out % 64 != 0 || n_out > (1 << 22) || (int64_t)batch * q_len * n_out > (1 << 28))
+    return 0;
+  return mla::oproj_workspace_bytes(batch * q_len, n_out, k_in);
+}
+
+mla_status mla_o_project(int32_t batch, int32_t q_len, int32_t k_in, int32_t n_out, const void* x, const void* w_o,
+                         void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_o || !y || !workspace) return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "a pointer is NULL");
+  if (batch < 1 || q_len < 1 || q_len > 8 || (int64_t)batch * q_len > (1 << 21))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "batch >= 1, q_len in [1, 8] and batch * q_len <= 2^21 are required");
+  if (k_in < 256 || k_in % 256 != 0 || k_in > (1 << 20) || n_out < 64 || n_out % 64 != 0 || n_out > (1 << 22) ||
+      (int64_t)batch * q_len * n_out > (1 << 28))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT,
+                         "k_in must be a multiple of 256 in [256, 2^20], n_out a multiple of 64 in [64, 2^22], and "
+                         "batch * q_len * n_out <= 2^28");
+  if (!mla::abi_aligned(x, 16) || !mla::abi_aligned(w_o, 16) || !mla::abi_aligned(workspace, 16) ||
+      !mla::abi_aligned(y, 8))
+    return mla::abi_fail(MLA_ERR_INVALID_ARGUMENT, "x, w_o and workspace must be 16-byte aligned, y 8-byte aligned");
+  const size_t need = mla::oproj_workspace_bytes(batch * q_len, n_out, k_in);
+  if (workspace_bytes < need) return mla::abi_fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than mla_o_project_workspace_bytes");
+  hipError_t e = mla::launch_o_project(batch * q_len, n_out, k_in, static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(w_o), static_cast<uint16_t*>(y),
+                                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return mla::abi_hip_fail(e, "output projection kernel launch");
+  mla::abi_ok();
+  return MLA_OK;
+}
+

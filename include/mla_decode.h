@@ -266,6 +266,23 @@ mla_status mla_decode_fp8_partials(const mla_plan* plan,
  *   [B, q_len, H, 512] (mla_decode's out), 16-byte aligned; w_uv: device bf16
  *   [H, 128, 512], 16-byte aligned; o: device bf16 [B, q_len, H, 128],
  *   8-byte aligned; batch * q_len <= 2^21.  One kernel.
+ *
+ * mla_o_project -- the output projection that closes the attention block
+ *   (the Huawei report's decode flow, section 3.2.1, ends MLA with it):
+ *     y[b, j, :] = W_O x[b, j, :],  x = the up-projected heads concatenated
+ *   in head order (mla_up_project's o viewed as [B * q_len, H * 128]).
+ *  x          device bf16 [B * q_len, k_in], 16-byte aligned (k_in = H * 128:
+ *             a multiple of 256 up to 2^20)
+ *  w_o        device bf16 [n_out, k_in] (row n = output n, as a linear layer
+ *             stores it), 16-byte aligned; n_out a multiple of 64 up to 2^22
+ *  y          device bf16 [B * q_len, n_out], 8-byte aligned
+ *  workspace  device, 16-byte aligned, at least
+ *             mla_o_project_workspace_bytes(batch, q_len, k_in, n_out) bytes
+ *             (fp32 partial sums over slices of k_in; contents not kept)
+ *  batch * q_len * n_out <= 2^28.  Two kernels (fp32 accumulation, the sum
+ *  rounded to bf16), no allocation, no synchronization.  Errors:
+ *  MLA_ERR_INVALID_ARGUMENT, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP.
+ *  mla_o_project_workspace_bytes returns 0 for sizes mla_o_project refuses.
  */
 enum { MLA_KV_BF16 = 0, MLA_KV_FP8 = 1 };
 mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads,
@@ -278,6 +295,10 @@ mla_status mla_prolog(int32_t batch, int32_t q_len, int32_t num_heads,
                       void* q_nope_absorbed, void* q_pe, void* stream);
 mla_status mla_up_project(int32_t batch, int32_t q_len, int32_t num_heads,
                           const float* attn_out, const void* w_uv, void* o, void* stream);
+size_t mla_o_project_workspace_bytes(int32_t batch, int32_t q_len, int32_t k_in, int32_t n_out);
+mla_status mla_o_project(int32_t batch, int32_t q_len, int32_t k_in, int32_t n_out,
+                         const void* x, const void* w_o, void* y,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Free a plan (its host memory and its device schedule).  NULL is a no-op.
  * The plan must not be in use by a kernel still running. */

@@ -268,3 +268,23 @@ def test_up_project_argument_checks():
     assert up(1, 1, 128, (1 << 40) + 8, f(), f(), None) == 1
     assert up(1, 1, 128, f(), (1 << 40) + 8, f(), None) == 1
     assert up(1, 1, 128, f(), f(), (1 << 40) + 4, None) == 1
+
+
+def test_o_project_argument_checks():
+    f = _Fake()
+    op, ws = mla.lib().mla_o_project, mla.lib().mla_o_project_workspace_bytes
+    need = ws(32, 1, 16384, 7168)
+    assert need == 4 * 32 * 7168 * 4  # 4 slices of fp32 partials
+    assert ws(64, 2, 16384, 7168) == 4 * 128 * 7168 * 4  # above 64 rows: 4 slices
+    assert ws(48, 1, 16384, 7168) == 8 * 48 * 7168 * 4  # 33..64 rows: 8 slices
+    assert ws(1, 1, 768, 64) == 2 * 1 * 64 * 4  # 6 chunks of 128: 4 does not divide them, 2 does
+    for bad in ((0, 1, 256, 64), (1, 9, 256, 64), (1, 1, 100, 64), (1, 1, 256, 96), (1, 1, 0, 64)):
+        assert ws(*bad) == 0, bad
+    args = lambda **o: [o.get(k, d) for k, d in (("B", 32), ("q", 1), ("K", 16384), ("N", 7168), ("x", f()), ("w", f()),
+                                                  ("y", f()), ("ws", f()), ("wsb", need), ("st", None))]
+    for over in (dict(x=None), dict(w=None), dict(y=None), dict(ws=None), dict(B=0), dict(q=9), dict(K=100),
+                 dict(K=0), dict(N=96), dict(N=0), dict(B=(1 << 17), N=(1 << 12) * 64),
+                 dict(x=(1 << 40) + 8), dict(w=(1 << 40) + 8), dict(ws=(1 << 40) + 8), dict(y=(1 << 40) + 4)):
+        assert op(*args(**over)) == 1, over
+    assert op(*args(wsb=need - 1)) == 3
+

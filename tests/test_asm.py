@@ -164,3 +164,22 @@ def test_projection_loads_issued_up_front(asm_prolog):
 def test_projection_loads_untouched_until_waited(asm_prolog):
     for body in asm_checks.kernel_bodies(asm_prolog, prefix=PROJ_PREFIX, whole=True):
         assert asm_checks.pending_load_violations(body) == []
+
+
+OPROJ_PREFIX = "_ZN3mla12_GLOBAL__N_112oproj_kernel"
+
+
+def test_output_projection_loads(asm_prolog):
+    """Per chunk: 32 rows x 128 columns: 2 X + 4 weight loads; 64 x 256: 8 + 8;
+    128 x 256: 16 + 8.  The first wait leaves the weights in flight; no
+    register of a pending load is touched."""
+    bodies = asm_checks.kernel_bodies(asm_prolog, prefix=OPROJ_PREFIX, whole=True)
+    assert len(bodies) == 3
+    seen = set()
+    for body in bodies:
+        n = sum(t.startswith("global_load_dwordx4") for t in body)
+        waits = sorted({int(t.split("vmcnt(")[1].split(")")[0]) for t in body if t.startswith("s_waitcnt") and "vmcnt" in t})
+        mfma = sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in body)
+        seen.add((n, tuple(waits), mfma))
+        assert asm_checks.pending_load_violations(body) == []
+    assert seen == {(6, (0, 4), 8), (16, (0, 8), 32), (24, (0, 8), 64)}, seen

@@ -1,5 +1,5 @@
 """The prolog (absorbed query, RoPE, RMSNorm, cache append) and the epilog (value
-up-projection) on an MI355X, through the C ABI, against the fp64 oracle.
+up-projection, output projection) on an MI355X, through the C ABI, against the fp64 oracle.
 
 Bars, derived from the arithmetic (fp32 inside the kernels, bf16 results):
   * a bf16 result r of an exact value v made of terms t_i (a dot product, a
@@ -9,6 +9,9 @@ Bars, derived from the arithmetic (fp32 inside the kernels, bf16 results):
     reciprocal square root;
   * the up-projection rounds its fp32 input to bf16 (2^-9 per term) before the
     MFMA: |r - v| <= 2^-8 |v| + 2^-8 sum|t_i|, and relative L2 <= 5e-3;
+  * the output projection sums K = H * 128 products in fp32 (MFMA chains, then
+    the slices' partials): |r - v| <= 2^-8 |v| + K 2^-24 sum|t_i|, and
+    relative L2 <= 5e-3;
   * FP8 rows: the E8M0 byte within one of the oracle's (the bf16 row may differ
     in its last bit), the decoded row within one E4M3 step (2^-3 relative, or
     the subnormal step) of the oracle's, and >= 98% of the codes bit-equal;
@@ -23,7 +26,14 @@ torch = pytest.importorskip("torch")
 
 import decode_attention_absorbed_amd as mla  # noqa: E402
 from oracle.mla_oracle_fp8 import e4m3_decode  # noqa: E402
-from oracle.mla_prolog_oracle import append_ref, bf16_round, prolog_ref, quantize_row_fp8, up_project_ref  # noqa: E402
+from oracle.mla_prolog_oracle import (  # noqa: E402
+    append_ref,
+    bf16_round,
+    o_project_ref,
+    prolog_ref,
+    quantize_row_fp8,
+    up_project_ref,
+)
 from tests import test_gpu_fp8 as t8  # noqa: E402
 from tests import test_gpu_parity as t16  # noqa: E402
 from workloads import (  # noqa: E402
@@ -262,6 +272,52 @@ def test_up_project_small(dev):
         assert rel <= 5e-3, f"up-projection rel-L2 {rel}"
 
 
+def check_o_project(o_bits, w_o_bits, y_bits, what):
+    """y against the oracle's output projection of the same bf16 inputs."""
+    o = bf16_bits_to_f64(o_bits)
+    w = bf16_bits_to_f64(w_o_bits)
+    exact = o_project_ref(o, w)
+    terms = o_project_ref(np.abs(o), np.abs(w))
+    K = w.shape[1]
+    check_bf16(y_bits, exact, terms, K * 2.0**-24, what)
+    got = bf16_bits_to_f64(y_bits)
+    rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+    assert rel <= 5e-3, f"{what}: rel-L2 {rel}"
+
+
+O_PROJ = [
+    # (batch, q_len, heads, n_out): K = 128 heads -> slices of 256 columns
+    (1, 1, 2, 64),  # K 256: one chunk, one slice
+    (3, 2, 4, 128),  # K 512: two slices
+    (37, 1, 16, 192),  # K 2048: eight slices; 37 rows (a ragged 16-row block)
+    (9, 8, 8, 64),  # 72 rows: 128-row chunks, four slices
+    (130, 1, 2, 64),  # 130 rows: two 128-row chunks
+    (5, 1, 6, 320),  # K 768: three chunks, one slice
+]
+
+
+@pytest.mark.parametrize("case", O_PROJ, ids=lambda c: f"B{c[0]}q{c[1]}H{c[2]}N{c[3]}")
+def test_o_project_small(dev, case):
+    B, q, H, N = case
+    rng = np.random.default_rng(31)
+    o = to_bf16_bits(rng.standard_normal((B, q, H, 128)).astype(np.float32))
+    w = to_bf16_bits((rng.standard_normal((N, H * 128)) / np.sqrt(H * 128)).astype(np.float32))
+    y = mla.mla_o_project(bf16_dev(o, dev), bf16_dev(w, dev))
+    torch.cuda.synchronize()
+    check_o_project(o, w, bits_of(y), f"o-projection B{B} q{q} H{H} N{N}")
+
+
+@pytest.mark.parametrize("name", ["dsv3", "mtp8"])
+def test_o_project_full_size(dev, name):
+    """7168 x 16384 weights at 32 and 128 query rows."""
+    x = make_config(name)
+    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=CONFIGS[name]["seed"] + 300, hidden=7168)
+    o = to_bf16_bits(np.random.default_rng(32).standard_normal((x.batch, x.q_len, x.heads, 128)).astype(np.float32))
+    y = mla.mla_o_project(bf16_dev(o, dev), bf16_dev(pi.w_o, dev))
+    torch.cuda.synchronize()
+    check_o_project(o, pi.w_o, bits_of(y), f"{name} o-projection")
+
+
 # ---- the chain: prolog -> decode -> up-projection against the oracle's chain ---------------
 
 
@@ -282,7 +338,9 @@ def _chain(dev, x, pi, fp8, idx=None):
             torch.from_numpy(x.seq_lens).to(dev), x.softmax_scale,
         )
     o = mla.mla_up_project(out, bf16_dev(pi.w_uv, dev))
+    y = None if pi.w_o is None else mla.mla_o_project(o, bf16_dev(pi.w_o, dev))
     torch.cuda.synchronize()
+    y = None if y is None else bf16_bits_to_f64(bits_of(y))
     out, lse, o = out.cpu().double().numpy(), lse.cpu().double().numpy(), bf16_bits_to_f64(bits_of(o))
     # the oracle's chain: its prolog, its rows appended, its decode on the
     # bf16 queries the decode entry takes, its up-projection
@@ -302,11 +360,13 @@ def _chain(dev, x, pi, fp8, idx=None):
         rms = s_abs = None
     sel = slice(None) if idx is None else np.asarray(idx)
     w = bf16_bits_to_f64(pi.w_uv)
-    return out[sel], lse[sel], o[sel], ref_o, ref_l, rms, s_abs, up_project_ref(ref_o, w)
+    ref_up = up_project_ref(ref_o, w)
+    ys = None if y is None else (y[sel], o_project_ref(ref_up, bf16_bits_to_f64(pi.w_o)))
+    return out[sel], lse[sel], o[sel], ref_o, ref_l, rms, s_abs, ref_up, ys
 
 
 def _check_chain(res, fp8, what):
-    out, lse, o, ref_o, ref_l, rms, s_abs, ref_up = res
+    out, lse, o, ref_o, ref_l, rms, s_abs, ref_up, ys = res
     if fp8:
         t8.compare(out, lse, ref_o, ref_l, rms, s_abs, what)
     else:
@@ -318,13 +378,20 @@ def _check_chain(res, fp8, what):
     # factor ~1 for errors not aligned with its rows; the bf16 roundings of the
     # up-projection add about 2^-9
     assert rel <= 2 * rel_out + 5e-3, f"{what}: up-projected rel-L2 {rel} (attention output's {rel_out})"
+    if ys is not None:
+        y, ref_y = ys
+        rel_y = float(np.linalg.norm(y - ref_y) / np.linalg.norm(ref_y))
+        print(f"{what} output projection: rel-L2 {rel_y:.3e}", flush=True)
+        # W_O (random, 7168 x 16384) mixes all heads: the error's relative
+        # size carries over as for W_UV, plus the output's own bf16 rounding
+        assert rel_y <= 2 * rel + 5e-3, f"{what}: output projection rel-L2 {rel_y} (up-projected {rel})"
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 def test_chain_small(dev, fp8):
     B, H, q, page, lens = 4, 16, 2, 16, [2, 30, 77, 140]
     x = (make_inputs_fp8 if fp8 else make_inputs)(B, H, q, page, lens, seed=21)
-    pi = make_prolog_inputs(B, q, H, x.seq_lens, seed=22)
+    pi = make_prolog_inputs(B, q, H, x.seq_lens, seed=22, hidden=256)
     _check_chain(_chain(dev, x, pi, fp8), fp8, f"chain {'fp8' if fp8 else 'bf16'}")
 
 
@@ -353,5 +420,5 @@ def test_chain_dsv3_sampled(dev, fp8):
     decode on 3 sampled requests."""
     c = CONFIGS["dsv3"]
     x = make_config_fp8("dsv3") if fp8 else make_config("dsv3")
-    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=c["seed"] + 200)
+    pi = make_prolog_inputs(x.batch, x.q_len, x.heads, x.seq_lens, seed=c["seed"] + 200, hidden=7168)
     _check_chain(_chain(dev, x, pi, fp8, idx=[0, 13, 31]), fp8, f"dsv3 chain {'fp8' if fp8 else 'bf16'}")
