@@ -429,14 +429,14 @@ hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const 
 // Split of K for the output projection: rows per chunk 32, 64 or 128 (the
 // smallest that holds every row: X's staging loads scale with it); columns
 // per chunk and slices (S at most, halved until it divides K into whole
-// chunks) from interleaved A/B runs at 7168 x 16384: 128 columns and 4 slices
-// for up to 32 rows, 256 and 8 up to 64, 256 and 4 above.  Narrower chunks
-// spread the concurrently read column offsets over more HBM channels; wider
-// ones (512) or fewer slices (2) were 35-60% slower.
+// chunks) from interleaved A/B runs at 7168 x 16384: 128 columns up to 64
+// rows, 256 above, 4 slices.  Narrower chunks spread the concurrently read
+// column offsets over more HBM channels; wider ones (512), narrower ones (64)
+// or fewer slices (2) were 30-60% slower, 8 or 16 slices 5-15% slower.
 void oproj_split(int32_t M, int32_t K, int* mc, int* S, int* kc) {
   *mc = M > 64 ? 128 : M > 32 ? 64 : 32;
-  *kc = *mc == 32 ? 128 : 256;
-  int s = M > 64 || M <= 32 ? 4 : 8;
+  *kc = *mc <= 64 ? 128 : 256;
+  int s = 4;
   while (s > 1 && (K / *kc) % s != 0) s >>= 1;
   *S = s;
 }
@@ -455,7 +455,7 @@ hipError_t launch_o_project(int32_t M, int32_t N, int32_t K, const uint16_t* x, 
   if (mc == 32)
     hipLaunchKernelGGL((oproj_kernel<32, 128>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   else if (mc == 64)
-    hipLaunchKernelGGL((oproj_kernel<64, 256>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+    hipLaunchKernelGGL((oproj_kernel<64, 128>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   else
     hipLaunchKernelGGL((oproj_kernel<128, 256>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   hipError_t e = hipGetLastError();

@@ -276,7 +276,7 @@ def test_o_project_argument_checks():
     need = ws(32, 1, 16384, 7168)
     assert need == 4 * 32 * 7168 * 4  # 4 slices of fp32 partials
     assert ws(64, 2, 16384, 7168) == 4 * 128 * 7168 * 4  # above 64 rows: 4 slices
-    assert ws(48, 1, 16384, 7168) == 8 * 48 * 7168 * 4  # 33..64 rows: 8 slices
+    assert ws(48, 1, 16384, 7168) == 4 * 48 * 7168 * 4
     assert ws(1, 1, 768, 64) == 2 * 1 * 64 * 4  # 6 chunks of 128: 4 does not divide them, 2 does
     for bad in ((0, 1, 256, 64), (1, 9, 256, 64), (1, 1, 100, 64), (1, 1, 256, 96), (1, 1, 0, 64)):
         assert ws(*bad) == 0, bad
