@@ -297,13 +297,14 @@ __global__ __launch_bounds__(256) void proj_kernel(int32_t M, int32_t H, const X
 // Output projection, split over K: slice s = blockIdx.y covers K columns
 // [s * kslice, +kslice); P[s][m][n] (fp32) = sum over the slice of
 // X[m, k] W[n, k].  Wave w of workgroup x owns output rows n in
-// [64 x + 16 w, +16) (lane l: row l%16, K slice 8(l/16) of each 32-wide step)
-// and query rows [MC z, +MC).  The slice is walked in KC-column chunks: the
-// chunk of X (its loads first) and the wave's KC / 32 weight fragments are issued
-// together as asm loads, X is staged in LDS as the MFMA's B operand, and the
-// 16-row blocks of X accumulate in registers.  Several workgroups per CU keep
-// the weight stream going while one of them computes.
-template <int MC, int KC>
+// [64 NA x + 16 NA w, +16 NA) (fragment a: lane l reads row 16a + l%16, K
+// slice 8(l/16) of each 32-wide step) and query rows [MC z, +MC).  The slice
+// is walked in KC-column chunks: the chunk of X (its loads first) and the
+// wave's NA * KC / 32 weight fragments are issued together as asm loads, X is
+// staged in LDS as the MFMA's B operand, and the 16-row blocks of X
+// accumulate in registers.  Several workgroups per CU keep the weight stream
+// going while one of them computes.
+template <int MC, int KC, int NA>
 __global__ __launch_bounds__(256) void oproj_kernel(int32_t M, int32_t N, int32_t K, int32_t kslice,
                                                     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                     float* __restrict__ P) {
@@ -314,12 +315,14 @@ __global__ __launch_bounds__(256) void oproj_kernel(int32_t M, int32_t N, int32_
   __shared__ __align__(16) uint16_t xs[MC * LDK];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int n0 = blockIdx.x * (64 * NA) + wave * (16 * NA);
   const int s = blockIdx.y, m0 = blockIdx.z * MC;
   const int rows = min(MC, M - m0);
-  f32x4 acc[MB];
+  f32x4 acc[NA][MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* wp = W + (size_t)(n0 + l16) * K + 8 * grp;
   // Workgroups of neighbouring row blocks walk their slice's chunks from
   // different starting points: all workgroups run at once, and in lockstep
@@ -334,10 +337,12 @@ __global__ __launch_bounds__(256) void oproj_kernel(int32_t M, int32_t N, int32_
       const int v = t + 256 * i, r = min(v / VPR, rows - 1);  // rows past the end repeat the last one
       xr[i] = load16(X + (size_t)(m0 + r) * K + kc + 8 * (v % VPR));
     }
-    bf16x8 w[KS];
+    bf16x8 w[NA][KS];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) w[j] = load16(wp + kc + 32 * j);
-    wait_vmem<KS>();  // X has arrived (loads complete in order); the weights stream on
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) w[a][j] = load16(wp + (size_t)16 * a * K + kc + 32 * j);
+    wait_vmem<NA * KS>();  // X has arrived (loads complete in order); the weights stream on
 #pragma unroll
     for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(xr[i]));
 #pragma unroll
@@ -348,24 +353,31 @@ __global__ __launch_bounds__(256) void oproj_kernel(int32_t M, int32_t N, int32_
     __syncthreads();
     wait_vmem<0>();
 #pragma unroll
-    for (int j = 0; j < KS; ++j) asm volatile("" : "+v"(w[j]));
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) asm volatile("" : "+v"(w[a][j]));
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       if (16 * b < rows) {
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
           const bf16x8 x = *reinterpret_cast<const bf16x8*>(xs + (16 * b + l16) * LDK + 32 * j + 8 * grp);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], x, acc[b], 0, 0, 0);
+#pragma unroll
+          for (int a = 0; a < NA; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[a][j], x, acc[a][b], 0, 0, 0);
         }
       }
     }
     __syncthreads();  // the next chunk overwrites xs
   }
-  // lane: outputs n0 + 4(l/16) + 0..3 of row 16b + l%16
+  // lane: outputs n0 + 16a + 4(l/16) + 0..3 of row 16b + l%16
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
     const int m = m0 + 16 * b + l16;
-    if (m < M) *reinterpret_cast<f32x4*>(P + ((size_t)s * M + m) * N + n0 + 4 * grp) = acc[b];
+    if (m < M)
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        *reinterpret_cast<f32x4*>(P + ((size_t)s * M + m) * N + n0 + 16 * a + 4 * grp) = acc[a][b];
   }
 }
 
@@ -426,38 +438,45 @@ hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const 
   return hipGetLastError();
 }
 
-// Split of K for the output projection: rows per chunk 32, 64 or 128 (the
-// smallest that holds every row: X's staging loads scale with it); columns
-// per chunk and slices (S at most, halved until it divides K into whole
-// chunks) from interleaved A/B runs at 7168 x 16384: 128 columns up to 64
-// rows, 256 above, 4 slices.  Narrower chunks spread the concurrently read
-// column offsets over more HBM channels; wider ones (512), narrower ones (64)
-// or fewer slices (2) were 30-60% slower, 8 or 16 slices 5-15% slower.
-void oproj_split(int32_t M, int32_t K, int* mc, int* S, int* kc) {
+// Shape of the output projection's launch, from interleaved A/B runs at
+// 7168 x 16384: query rows per chunk 32, 64 or 128 (the smallest that holds
+// every row: X's staging loads scale with it); up to 64 rows, 128 output rows
+// per workgroup when N allows (X's chunks, re-read by every workgroup, then
+// serve twice the rows) with 8 slices of K, else 64 with 4 slices, and
+// 128-column chunks; above 64 rows, 64 output rows, 256-column chunks and 4
+// slices.  Narrower chunks spread the concurrently
+// read column offsets over more HBM channels.  S is halved until it divides K
+// into whole chunks.
+void oproj_split(int32_t M, int32_t N, int32_t K, int* mc, int* S, int* kc, int* na) {
   *mc = M > 64 ? 128 : M > 32 ? 64 : 32;
   *kc = *mc <= 64 ? 128 : 256;
-  int s = 4;
+  *na = *mc <= 64 && N % 128 == 0 ? 2 : 1;
+  int s = *na == 2 ? 8 : 4;
   while (s > 1 && (K / *kc) % s != 0) s >>= 1;
   *S = s;
 }
 
 size_t oproj_workspace_bytes(int32_t M, int32_t N, int32_t K) {
-  int mc, S, kc;
-  oproj_split(M, K, &mc, &S, &kc);
+  int mc, S, kc, na;
+  oproj_split(M, N, K, &mc, &S, &kc, &na);
   return (size_t)S * M * N * sizeof(float);
 }
 
 hipError_t launch_o_project(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint16_t* w, uint16_t* y,
                             float* partials, hipStream_t stream) {
-  int mc, S, kc;
-  oproj_split(M, K, &mc, &S, &kc);
-  const dim3 grid(N / 64, S, (M + mc - 1) / mc);
-  if (mc == 32)
-    hipLaunchKernelGGL((oproj_kernel<32, 128>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  int mc, S, kc, na;
+  oproj_split(M, N, K, &mc, &S, &kc, &na);
+  const dim3 grid(N / (64 * na), S, (M + mc - 1) / mc);
+  if (mc == 32 && na == 2)
+    hipLaunchKernelGGL((oproj_kernel<32, 128, 2>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  else if (mc == 32)
+    hipLaunchKernelGGL((oproj_kernel<32, 128, 1>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+  else if (mc == 64 && na == 2)
+    hipLaunchKernelGGL((oproj_kernel<64, 128, 2>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   else if (mc == 64)
-    hipLaunchKernelGGL((oproj_kernel<64, 128>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+    hipLaunchKernelGGL((oproj_kernel<64, 128, 1>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   else
-    hipLaunchKernelGGL((oproj_kernel<128, 256>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
+    hipLaunchKernelGGL((oproj_kernel<128, 256, 1>), grid, dim3(256), 0, stream, M, N, K, K / S, x, w, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mn4 = (int64_t)M * N / 4;

@@ -274,10 +274,12 @@ def test_o_project_argument_checks():
     f = _Fake()
     op, ws = mla.lib().mla_o_project, mla.lib().mla_o_project_workspace_bytes
     need = ws(32, 1, 16384, 7168)
-    assert need == 4 * 32 * 7168 * 4  # 4 slices of fp32 partials
+    assert need == 8 * 32 * 7168 * 4  # 8 slices of fp32 partials (128 output rows per workgroup)
     assert ws(64, 2, 16384, 7168) == 4 * 128 * 7168 * 4  # above 64 rows: 4 slices
-    assert ws(48, 1, 16384, 7168) == 4 * 48 * 7168 * 4
-    assert ws(1, 1, 768, 64) == 2 * 1 * 64 * 4  # 6 chunks of 128: 4 does not divide them, 2 does
+    assert ws(48, 1, 16384, 7168) == 8 * 48 * 7168 * 4
+    assert ws(48, 1, 16384, 7104) == 4 * 48 * 7104 * 4  # 7104 = 111 x 64: 64 output rows, 4 slices
+    assert ws(1, 1, 768, 64) == 2 * 1 * 64 * 4  # 64 outputs: 4 slices wanted, 6 chunks of 128 -> 2
+    assert ws(1, 1, 768, 128) == 2 * 1 * 128 * 4  # 128 outputs: 8 slices wanted -> 2
     for bad in ((0, 1, 256, 64), (1, 9, 256, 64), (1, 1, 100, 64), (1, 1, 256, 96), (1, 1, 0, 64)):
         assert ws(*bad) == 0, bad
     args = lambda **o: [o.get(k, d) for k, d in (("B", 32), ("q", 1), ("K", 16384), ("N", 7168), ("x", f()), ("w", f()),

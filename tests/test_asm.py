@@ -170,11 +170,12 @@ OPROJ_PREFIX = "_ZN3mla12_GLOBAL__N_112oproj_kernel"
 
 
 def test_output_projection_loads(asm_prolog):
-    """Per chunk: 32 rows x 128 columns: 2 X + 4 weight loads; 64 x 128: 4 + 4;
-    128 x 256: 16 + 8.  The first wait leaves the weights in flight; no
-    register of a pending load is touched."""
+    """Per chunk and lane: X loads (32 or 64 query rows x 128 columns: 2 or 4;
+    128 x 256: 16) + weight loads (128 output rows per workgroup: 2 x 4; 64:
+    4 or 8); the first wait leaves the weights in flight; no register of a
+    pending load is touched."""
     bodies = asm_checks.kernel_bodies(asm_prolog, prefix=OPROJ_PREFIX, whole=True)
-    assert len(bodies) == 3
+    assert len(bodies) == 5
     seen = set()
     for body in bodies:
         n = sum(t.startswith("global_load_dwordx4") for t in body)
@@ -182,4 +183,4 @@ def test_output_projection_loads(asm_prolog):
         mfma = sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in body)
         seen.add((n, tuple(waits), mfma))
         assert asm_checks.pending_load_violations(body) == []
-    assert seen == {(6, (0, 4), 8), (8, (0, 4), 16), (24, (0, 8), 64)}, seen
+    assert seen == {(10, (0, 8), 16), (12, (0, 8), 32), (6, (0, 4), 8), (8, (0, 4), 16), (24, (0, 8), 64)}, seen

@@ -292,7 +292,9 @@ O_PROJ = [
     (37, 1, 16, 192),  # K 2048: eight slices; 37 rows (a ragged 16-row block)
     (9, 8, 8, 64),  # 72 rows: 128-row chunks, four slices
     (130, 1, 2, 64),  # 130 rows: two 128-row chunks
-    (5, 1, 6, 320),  # K 768: three chunks, one slice
+    (5, 1, 6, 320),  # K 768: six chunks, two slices; 320 outputs: 64 per workgroup
+    (2, 1, 4, 256),  # 128 outputs per workgroup
+    (40, 1, 2, 384),  # 40 rows (64-row chunks), 128 outputs per workgroup
 ]
 
 
