@@ -1,12 +1,13 @@
 // The steps next to the decode attention, for gfx950: the absorbed-query
-// projection, RoPE, the new tokens' cache rows (prolog) and the value
-// up-projection (epilog).
+// projection, RoPE, the new tokens' cache rows (prolog), the value
+// up-projection and the output projection (epilog).
 //
 // The Huawei report ("DeepSeek V3/R1 inference deployment best practices on
 // Ascend servers", section 6.1, the operators before MLA) absorbs the weights
 // and fuses the decode prolog into one operator; the CloudMatrix384 digest
 // (its MLA optimization paragraph) names RMSNorm, the projections and RoPE as
-// its parts.  Here:
+// its parts; the report's decode flow (section 3.2.1) closes MLA with the
+// output projection.  Here:
 //  * proj_kernel: Y[m, h, :] = W[h] X[m, h, :] per head (W[h] is N x K, rows
 //    contiguous in K), bound by the weights' bytes.  Absorption: X = q_nope
 //    (128), W = W_UK^T (512 x 128), Y = q_nope_absorbed (bf16).
