@@ -187,6 +187,8 @@ SMALL = [
     (2, 128, 1, 64, [64, 65]),
     (5, 8, 4, 16, [4, 16, 19, 33, 100]),
     (37, 2, 1, 16, list(range(1, 38))),  # 37 query rows: a ragged 32-row block
+    (70, 4, 2, 16, list(range(2, 72))),  # 140 query rows: two 128-row chunks; 4 heads, so each
+                                         # per-token workgroup appends 32 or 3 tokens
 ]
 
 
