@@ -766,9 +766,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 // 32(l/4) + 16 + 4(l%4) + e - 4 otherwise.  All waves derive
 // lse = logsumexp_s lse_s for the row; the partial weights
 // exp(lse_s - lse) f_s go to LDS in chunks of kCombineChunk; wave j (0..3)
-// then sums the partials s = j, j+4, ... of the chunk, and the four waves'
-// sums meet in LDS.
+// then sums the partials s = j, j+4, ... of the chunk, kCombineBatch loads at
+// a time, and the four waves' sums meet in LDS.
 constexpr int kCombineChunk = 256;
+constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restrict__ jobs,
                                                        const uint16_t* __restrict__ ws_o,
                                                        const float* __restrict__ ws_lse,
@@ -785,18 +786,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
   const int rb = row / rpb, rl = row - rb * rpb;
   auto ri_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
 
+  // The partials' lse values, four per lane in flight at once (indices past
+  // the end load the last one again and are masked).
   float m = -INFINITY;
   bool any_nan = false;  // fmaxf drops NaN; a NaN partial (length mismatch) must stay loud
-  for (int s = lane; s < job.n; s += 64) {
-    const float x = ws_lse[ri_of(s)];
-    any_nan |= (x != x);
-    m = fmaxf(m, x);
+  for (int s0 = 0; s0 < job.n; s0 += 256) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = ws_lse[ri_of(min(s0 + lane + 64 * i, job.n - 1))];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + lane + 64 * i < job.n) {
+        any_nan |= (x[i] != x[i]);
+        m = fmaxf(m, x[i]);
+      }
   }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   any_nan = __any(any_nan);
   float z = 0.f;
   if (m != -INFINITY)
-    for (int s = lane; s < job.n; s += 64) z += __expf(ws_lse[ri_of(s)] - m);
+    for (int s0 = 0; s0 < job.n; s0 += 256) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = ws_lse[ri_of(min(s0 + lane + 64 * i, job.n - 1))];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s0 + lane + 64 * i < job.n) z += __expf(x[i] - m);
+    }
   for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
   const float lse_v = any_nan ? NAN : (m == -INFINITY ? -INFINITY : m + __logf(z));
   const bool live = !any_nan && m != -INFINITY;
@@ -810,12 +826,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
         wts[threadIdx.x] = __expf(ws_lse[ri] - lse_v) * ws_f[ri];
       }
       __syncthreads();
-#pragma unroll 4
-      for (int k = wv; k < cn; k += 4) {
-        const float w = wts[k];
-        const f16x8 v = *reinterpret_cast<const f16x8*>(ws_o + ri_of(c0 + k) * 512 + 8 * lane);
-        acc0 += w * f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        acc1 += w * f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+      // kCombineBatch partials per wave in flight at once (past the chunk's
+      // end the last one is loaded again with weight 0), so a wave's share
+      // of the chunk costs a few round trips, not one per partial.
+      for (int k0 = wv; k0 < cn; k0 += 4 * kCombineBatch) {
+        f16x8 v[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+          const int k = min(k0 + 4 * i, cn - 1);
+          v[i] = *reinterpret_cast<const f16x8*>(ws_o + ri_of(c0 + k) * 512 + 8 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+          const int k = k0 + 4 * i;
+          const float w = k < cn ? wts[k] : 0.f;
+          acc0 += w * f32x4{(float)v[i][0], (float)v[i][1], (float)v[i][2], (float)v[i][3]};
+          acc1 += w * f32x4{(float)v[i][4], (float)v[i][5], (float)v[i][6], (float)v[i][7]};
+        }
       }
       __syncthreads();
     }
