@@ -36,3 +36,17 @@ def test_roofline_binding_side():
     assert r2["bound"] == "hbm"
     r3 = acc.roofline_seconds([4608] * 64, 128, 2, 64)
     assert r3["bound"] == "mfma"
+
+
+def test_projection_bytes_by_hand():
+    from decode_attention_absorbed_amd import accounting as acc
+
+    # dsv3 step: 32 query rows, 128 heads
+    w = 128 * 128 * 512 * 2  # one of W_UK / W_UV: 16.8 MB
+    assert acc.up_project_bytes(32, 128) == w + 32 * 128 * (512 * 4 + 128 * 2)
+    per_head = 32 * 128 * (128 * 2 + 512 * 2 + 2 * 64 * 2)  # q_nope in, q_abs out, q_pe in + out
+    per_token = 32 * ((512 + 64) * 2 + 1152 + 64 * 4 + 4 + 4)  # c_kv + k_pe in, row out, table row, len, page id
+    assert acc.prolog_bytes(32, 128) == w + per_head + per_token + 512 * 2
+    assert acc.prolog_bytes(32, 128, "fp8") == acc.prolog_bytes(32, 128) - 32 * (1152 - 577)
+    assert acc.o_project_bytes(32, 128) == 7168 * 16384 * 2 + 32 * (16384 + 7168) * 2  # 236.4 MB
+    assert round(acc.o_project_bytes(32, 128) / 1e6, 1) == 236.4

@@ -45,3 +45,27 @@ def test_seeded_determinism():
     for f in ("q_nope", "q_pe", "cache", "block_table", "seq_lens"):
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
     assert set(CONFIGS) == {"tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"}
+
+
+def test_prolog_inputs_structure_and_determinism():
+    import numpy as np
+
+    from workloads import bf16_bits_to_f64, make_prolog_inputs
+
+    a = make_prolog_inputs(3, 2, 4, [5, 9, 17], seed=3, hidden=64)
+    b = make_prolog_inputs(3, 2, 4, [5, 9, 17], seed=3, hidden=64)
+    c = make_prolog_inputs(3, 2, 4, [5, 9, 17], seed=3)
+    assert a.q_nope128.shape == (3, 2, 4, 128) and a.q_pe_raw.shape == (3, 2, 4, 64)
+    assert a.w_uk_t.shape == (4, 512, 128) and a.w_uv.shape == (4, 128, 512) and a.w_o.shape == (64, 512)
+    assert a.c_kv_raw.shape == (3, 2, 512) and a.k_pe_raw.shape == (3, 2, 64) and a.kv_norm_w.shape == (512,)
+    assert a.rope_cos_sin.shape == (18, 64) and a.rope_cos_sin.dtype == np.float32
+    for k in ("q_nope128", "q_pe_raw", "w_uk_t", "c_kv_raw", "kv_norm_w", "k_pe_raw", "w_uv", "w_o"):
+        assert np.array_equal(getattr(a, k), getattr(b, k)), k
+    # W_O is drawn last: asking for it leaves every other draw unchanged
+    assert c.w_o is None and np.array_equal(c.w_uv, a.w_uv)
+    # the RoPE table is cos then sin of p * 10000^(-2i/64)
+    p, i = 7, 5
+    ang = p * 10000.0 ** (-2 * i / 64)
+    assert abs(a.rope_cos_sin[p, i] - np.cos(ang)) < 1e-6 and abs(a.rope_cos_sin[p, 32 + i] - np.sin(ang)) < 1e-6
+    # W_UK^T's transpose is the [H, 128, 512] W_UK
+    assert np.array_equal(a.w_uk_f64()[1, 3, 7], bf16_bits_to_f64(a.w_uk_t)[1, 7, 3])
