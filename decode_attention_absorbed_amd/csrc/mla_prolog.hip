@@ -413,8 +413,16 @@ hipError_t launch_prolog(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_
   const PrologArgs pa{q_len,   q_pe_raw,    c_kv_raw,  norm_w,    eps,       k_pe_raw, cos_sin, max_pos,
                       seq_lens, block_table, bt_stride, num_pages, page_log2, cache,    scales,  q_pe_out};
   constexpr int NA = 2;
-  const dim3 grid(512 / (64 * NA) + 1, H, (M + kAbsorbRows - 1) / kAbsorbRows);
-  if (fp8)
+  // 32-row chunks up to 32 rows: X's staging loads scale with the chunk
+  const int mc = M <= 32 ? 32 : kAbsorbRows;
+  const dim3 grid(512 / (64 * NA) + 1, H, (M + mc - 1) / mc);
+  if (mc == 32 && fp8)
+    hipLaunchKernelGGL((proj_kernel<uint16_t, 128, 512, NA, 32, 1>), grid, dim3(256), 0, stream, M, H, q_nope, w_uk_t,
+                       q_abs, pa);
+  else if (mc == 32)
+    hipLaunchKernelGGL((proj_kernel<uint16_t, 128, 512, NA, 32, 0>), grid, dim3(256), 0, stream, M, H, q_nope, w_uk_t,
+                       q_abs, pa);
+  else if (fp8)
     hipLaunchKernelGGL((proj_kernel<uint16_t, 128, 512, NA, kAbsorbRows, 1>), grid, dim3(256), 0, stream, M, H,
                        q_nope, w_uk_t, q_abs, pa);
   else
@@ -426,7 +434,11 @@ hipError_t launch_prolog(int32_t B, int32_t q_len, int32_t H, const uint16_t* q_
 hipError_t launch_up_project(int32_t M, int32_t H, const float* attn_out, const uint16_t* w_uv, uint16_t* o,
                              hipStream_t stream) {
   const PrologArgs none{};
-  if (M <= 64) {
+  if (M <= 32) {
+    // two workgroups per head (64 outputs each), all rows in one 32-row chunk
+    hipLaunchKernelGGL((proj_kernel<float, 512, 128, 1, 32, -1>), dim3(2, H, 1), dim3(256), 0, stream, M, H, attn_out,
+                       w_uv, o, none);
+  } else if (M <= 64) {
     // two workgroups per head (64 outputs each), all rows in one chunk
     hipLaunchKernelGGL((proj_kernel<float, 512, 128, 1, 64, -1>), dim3(2, H, 1), dim3(256), 0, stream, M, H, attn_out,
                        w_uv, o, none);

@@ -139,15 +139,15 @@ def asm_prolog(tmp_path_factory):
 
 
 def test_projection_loads_issued_up_front(asm_prolog):
-    """absorption (bf16 cache, FP8 cache): 8 X + 8 weight loads per lane;
-    up-projection: 32 X + 16 weight loads (64-row chunks, 64 outputs per
-    workgroup) or 16 X + 32 weight loads (32-row chunks, 128 outputs); the
-    first wait leaves the weights in flight, the second drains them before
-    the MFMAs."""
+    """Absorption (bf16 and FP8 cache; 32- or 128-row chunks): 2 or 8 X loads +
+    8 weight loads per lane; up-projection: 16 X + 16 weight loads (32-row
+    chunks), 32 + 16 (64-row chunks, 64 outputs per workgroup) or 16 + 32
+    (32-row chunks, 128 outputs); the first wait leaves the weights in flight,
+    the second drains them before the MFMAs."""
     bodies = asm_checks.kernel_bodies(asm_prolog, prefix=PROJ_PREFIX, whole=True)
-    assert len(bodies) == 4
+    assert len(bodies) == 7
+    seen = set()
     for body in bodies:
-        n = sum(t.startswith("global_load_dwordx4") and t.split(";")[0].rstrip().endswith("off") for t in body)
         first = next(i for i, t in enumerate(body) if t.startswith("global_load_dwordx4"))
         run = 0
         for t in body[first:]:
@@ -157,8 +157,9 @@ def test_projection_loads_issued_up_front(asm_prolog):
                 break
             run += 1
         waits = [int(t.split("vmcnt(")[1].split(")")[0]) for t in body if t.startswith("s_waitcnt") and "vmcnt" in t]
-        assert (run, waits[:2]) in ((16, [8, 0]), (48, [16, 0]), (48, [32, 0])), (run, waits[:4], n)
-        assert sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in body) in (8, 16, 32)
+        mfma = sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in body)
+        seen.add((run, tuple(waits[:2]), mfma))
+    assert seen == {(10, (8, 0), 8), (16, (8, 0), 8), (32, (16, 0), 16), (48, (16, 0), 16), (48, (32, 0), 32)}, seen
 
 
 def test_projection_loads_untouched_until_waited(asm_prolog):
