@@ -32,6 +32,7 @@ MLA_Q_NUM_PARTIALS = 2
 MLA_Q_ROWS_PER_BLOCK = 3
 MLA_Q_TILE_TOKENS = 4
 MLA_Q_NUM_ROW_BLOCKS = 5
+MLA_Q_NUM_COMBINE_WGS = 6
 
 #: every symbol include/mla_decode.h declares
 EXPORTED = (
@@ -46,6 +47,7 @@ EXPORTED = (
     "mla_last_error",
     "mla_plan_query",
     "mla_plan_copy",
+    "mla_plan_copy_combine",
     "mla_decode_fp8_plan",
     "mla_decode_fp8_plan_host",
     "mla_decode_fp8",
@@ -109,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.mla_plan_query.restype = ctypes.c_int64
     L.mla_plan_copy.argtypes = [vp, i32p, i32p]
     L.mla_plan_copy.restype = ctypes.c_int
+    L.mla_plan_copy_combine.argtypes = [vp, i32p]
+    L.mla_plan_copy_combine.restype = ctypes.c_int
     L.mla_decode_fp8_plan.argtypes = L.mla_decode_plan.argtypes
     L.mla_decode_fp8_plan.restype = ctypes.c_int
     L.mla_decode_fp8_plan_host.argtypes = L.mla_decode_plan.argtypes
@@ -175,6 +179,13 @@ class Plan:
         wg = np.zeros((max(n, 1), 4), dtype=np.int32)
         _check(lib().mla_plan_copy(self.handle, None, wg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return wg[:n]
+
+    def combine_units(self) -> np.ndarray:
+        """int32 [combine grid, 4]: request, first partial, pieces (0 = empty), first row."""
+        n = self.query(MLA_Q_NUM_COMBINE_WGS)
+        cu = np.zeros((max(n, 1), 4), dtype=np.int32)
+        _check(lib().mla_plan_copy_combine(self.handle, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return cu[:n]
 
     def destroy(self) -> None:
         if self.handle:

@@ -761,7 +761,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
   }
 }
 
-// One workgroup = one row of one split request.  Stored position 8l + e of a
+// One workgroup = one row of one split request (the unit's row0).  Stored position 8l + e of a
 // row (lane l) holds column 32(l/4) + 4(l%4) + e for e < 4 and
 // 32(l/4) + 16 + 4(l%4) + e - 4 otherwise.  All waves derive
 // lse = logsumexp_s lse_s for the row; the partial weights
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 // a time, and the four waves' sums meet in LDS.
 constexpr int kCombineChunk = 256;
 constexpr int kCombineBatch = 16;
-__global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restrict__ jobs,
+__global__ __launch_bounds__(256) void combine_kernel(const CombineUnit* __restrict__ units,
                                                        const uint16_t* __restrict__ ws_o,
                                                        const float* __restrict__ ws_lse,
                                                        const float* __restrict__ ws_f, int32_t rows, int32_t rpb,
@@ -779,8 +779,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   __shared__ float wts[kCombineChunk];
   __shared__ f32x4 red[3][64][2];
-  const CombineJob job = jobs[blockIdx.x];
-  const int row = blockIdx.y;
+  const CombineUnit job = units[blockIdx.x];
+  if (job.n == 0) return;
+  const int row = job.row0;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int rb = row / rpb, rl = row - rb * rpb;
@@ -870,22 +871,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineJob* __restri
 }
 
 // Combine for requests split into at most kCombineSmallMax pieces: one wave
-// per row (4 rows per workgroup).  Lane l owns stored positions 8l .. 8l+7 (as
+// per row (kCombineSmallRows rows per workgroup, from the unit's row0).  Lane l owns stored positions 8l .. 8l+7 (as
 // in combine_kernel); every partial value of the row and the per-partial lse
 // and scale (lane s holds partial s) are loaded at once, so the row costs one
 // memory round trip.  Weights exp(lse_s - lse) f_s are broadcast from lane s.
-constexpr int kCombineSmallMax = 16;
-__global__ __launch_bounds__(256) void combine_small_kernel(const CombineJob* __restrict__ jobs,
+__global__ __launch_bounds__(64 * kCombineSmallRows) void combine_small_kernel(const CombineUnit* __restrict__ units,
                                                              const uint16_t* __restrict__ ws_o,
                                                              const float* __restrict__ ws_lse,
                                                              const float* __restrict__ ws_f, int32_t rows,
                                                              int32_t rpb, int32_t nrb, float* __restrict__ out,
                                                              float* __restrict__ lse) {
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  const CombineJob job = jobs[blockIdx.x];
+  const CombineUnit job = units[blockIdx.x];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int row = job.row0 + (threadIdx.x >> 6);
+  if (job.n == 0 || row >= rows) return;
   const int rb = row / rpb, rl = row - rb * rpb;
   auto ri_of = [&](int s) { return ((int64_t)(job.p0 + s) * nrb + rb) * rpb + rl; };
   const int n = job.n;  // <= kCombineSmallMax (checked on the host)
@@ -934,8 +934,8 @@ __global__ __launch_bounds__(256) void combine_small_kernel(const CombineJob* __
 
 struct mla_plan {
   mla::PlanData d;
-  void* dev = nullptr;  // device schedule: segs | wgs | jobs | planned lens
-  size_t off_segs = 0, off_wgs = 0, off_jobs = 0, off_lens = 0;
+  void* dev = nullptr;  // device schedule: segs | wgs | combine units | planned lens
+  size_t off_segs = 0, off_wgs = 0, off_units = 0, off_lens = 0;
   int device = -1;
 };
 
@@ -997,13 +997,14 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
     const mla::PlanData& d = p->d;
     p->off_segs = 0;
     p->off_wgs = align256(d.segs.size() * sizeof(mla::Segment));
-    p->off_jobs = p->off_wgs + align256(d.wgs.size() * sizeof(mla::WorkgroupRange));
-    p->off_lens = p->off_jobs + align256(d.jobs.size() * sizeof(mla::CombineJob));
+    p->off_units = p->off_wgs + align256(d.wgs.size() * sizeof(mla::WorkgroupRange));
+    p->off_lens = p->off_units + align256(d.cunits.size() * sizeof(mla::CombineUnit));
     const size_t total = p->off_lens + align256(d.lens.size() * sizeof(int32_t));
     std::string host(total, '\0');
     std::memcpy(&host[p->off_segs], d.segs.data(), d.segs.size() * sizeof(mla::Segment));
     std::memcpy(&host[p->off_wgs], d.wgs.data(), d.wgs.size() * sizeof(mla::WorkgroupRange));
-    if (!d.jobs.empty()) std::memcpy(&host[p->off_jobs], d.jobs.data(), d.jobs.size() * sizeof(mla::CombineJob));
+    if (!d.cunits.empty())
+      std::memcpy(&host[p->off_units], d.cunits.data(), d.cunits.size() * sizeof(mla::CombineUnit));
     std::memcpy(&host[p->off_lens], d.lens.data(), d.lens.size() * sizeof(int32_t));
     hipError_t e = hipMalloc(&p->dev, total);
     if (e != hipSuccess) {
@@ -1134,6 +1135,7 @@ int64_t mla_plan_query(const mla_plan* plan, int32_t key) {
     case MLA_Q_ROWS_PER_BLOCK: return d.v.rows_per_block();
     case MLA_Q_TILE_TOKENS: return d.v.tile_tokens;
     case MLA_Q_NUM_ROW_BLOCKS: return d.nrb;
+    case MLA_Q_NUM_COMBINE_WGS: return d.jobs.empty() ? 0 : (int64_t)d.cunits.size();
   }
   return -1;
 }
@@ -1154,6 +1156,19 @@ mla_status mla_plan_copy(const mla_plan* plan, int32_t* seg, int32_t* wg) {
       wg[4 * i + 1] = d.wgs[i].seg_end;
       wg[4 * i + 2] = d.wgs[i].row_block;
       wg[4 * i + 3] = 0;
+    }
+  return MLA_OK;
+}
+
+mla_status mla_plan_copy_combine(const mla_plan* plan, int32_t* unit) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const mla::PlanData& d = plan->d;
+  if (unit && !d.jobs.empty())
+    for (size_t i = 0; i < d.cunits.size(); ++i) {
+      unit[4 * i + 0] = d.cunits[i].b;
+      unit[4 * i + 1] = d.cunits[i].p0;
+      unit[4 * i + 2] = d.cunits[i].n;
+      unit[4 * i + 3] = d.cunits[i].row0;
     }
   return MLA_OK;
 }
@@ -1210,14 +1225,14 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void
   const mla::PlanData& d = plan->d;
   if (!d.jobs.empty()) {
     const char* base = static_cast<const char*>(plan->dev);
-    const mla::CombineJob* jobs = reinterpret_cast<const mla::CombineJob*>(base + plan->off_jobs);
+    const mla::CombineUnit* units = reinterpret_cast<const mla::CombineUnit*>(base + plan->off_units);
     if (d.max_pieces <= mla::kCombineSmallMax)
-      hipLaunchKernelGGL(mla::combine_small_kernel, dim3((unsigned)d.jobs.size(), (unsigned)((d.rows + 3) / 4)),
-                         dim3(256), 0, static_cast<hipStream_t>(stream), jobs, ws.o, ws.lse, ws.f, d.rows,
-                         d.v.rows_per_block(), d.nrb, out, lse);
+      hipLaunchKernelGGL(mla::combine_small_kernel, dim3((unsigned)d.cunits.size()), dim3(64 * mla::kCombineSmallRows),
+                         0, static_cast<hipStream_t>(stream), units, ws.o, ws.lse, ws.f, d.rows, d.v.rows_per_block(),
+                         d.nrb, out, lse);
     else
-      hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.jobs.size(), (unsigned)d.rows), dim3(256), 0,
-                         static_cast<hipStream_t>(stream), jobs, ws.o, ws.lse, ws.f, d.rows, d.v.rows_per_block(),
+      hipLaunchKernelGGL(mla::combine_kernel, dim3((unsigned)d.cunits.size()), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), units, ws.o, ws.lse, ws.f, d.rows, d.v.rows_per_block(),
                          d.nrb, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

@@ -182,6 +182,7 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
       }
   p.num_partials = np;
 
+  std::vector<int32_t> slot_of_partial(np, 0);
   std::vector<std::pair<int32_t, int32_t>> slot_range(S);  // [begin, end) in segs
   for (int32_t s = 0; s < S; ++s) {
     slot_range[s].first = (int32_t)p.segs.size();
@@ -191,6 +192,7 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
       g.kv_begin = pc.t0 * T;
       g.kv_end = std::min(pc.t1 * T, lens[pc.b]);
       g.partial = pieces_of[pc.b] > 1 ? first_partial[pc.b] + next_partial[pc.b]++ : -1;
+      if (g.partial >= 0) slot_of_partial[g.partial] = s;
       p.segs.push_back(g);
     }
     slot_range[s].second = (int32_t)p.segs.size();
@@ -220,6 +222,43 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
       p.jobs.push_back(CombineJob{b, first_partial[b], pieces_of[b], 0});
       p.max_pieces = std::max(p.max_pieces, pieces_of[b]);
     }
+
+  // Combine workgroups.  The partials of one (request, row block) were
+  // written by the workgroups of its pieces, on the XCDs chosen above; the
+  // combine workgroup that reads them goes to the XCD that wrote most of them,
+  // so that its reads can hit that XCD's L2.  Each XCD takes at most an even
+  // share; the rest go to the XCDs with the fewest.
+  if (!p.jobs.empty()) {
+    const int32_t per_unit = p.max_pieces <= kCombineSmallMax ? kCombineSmallRows : 1;
+    const int32_t rpb = p.v.rows_per_block();
+    const size_t units = p.jobs.size() * (size_t)((p.rows + per_unit - 1) / per_unit);
+    const size_t cap = (units + kNumXcd - 1) / kNumXcd;
+    std::vector<std::vector<CombineUnit>> lists(kNumXcd);
+    std::vector<CombineUnit> spill;
+    for (const CombineJob& j : p.jobs)
+      for (int32_t r0 = 0; r0 < p.rows; r0 += per_unit) {
+        const int64_t rb = r0 / rpb;
+        int32_t votes[kNumXcd] = {};
+        for (int32_t k = 0; k < j.n; ++k) votes[((slot_of_partial[j.p0 + k] * p.nrb + rb) / K) % kNumXcd]++;
+        const int32_t x = (int32_t)(std::max_element(votes, votes + kNumXcd) - votes);
+        const CombineUnit cu{j.b, j.p0, j.n, r0};
+        if (lists[x].size() < cap)
+          lists[x].push_back(cu);
+        else
+          spill.push_back(cu);
+      }
+    for (const CombineUnit& cu : spill) {
+      auto it = std::min_element(lists.begin(), lists.end(),
+                                 [](const std::vector<CombineUnit>& a, const std::vector<CombineUnit>& b) {
+                                   return a.size() < b.size();
+                                 });
+      it->push_back(cu);
+    }
+    p.cunits.assign(cap * kNumXcd, CombineUnit{0, 0, 0, 0});
+    for (int32_t x = 0; x < kNumXcd; ++x)
+      for (size_t i = 0; i < lists[x].size(); ++i) p.cunits[i * kNumXcd + x] = lists[x][i];
+    while (!p.cunits.empty() && p.cunits.back().n == 0) p.cunits.pop_back();
+  }
   return kOk;
 }
 

@@ -26,6 +26,13 @@ struct CombineJob {
   int32_t b, p0, n, pad;
 };
 
+// One combine workgroup: rows row0 .. row0 + kCombineSmallRows - 1 (short
+// kernel) or row row0 (long kernel) of request b, whose pieces are partials
+// p0 .. p0 + n - 1.  n = 0 marks an empty launch slot.
+struct CombineUnit {
+  int32_t b, p0, n, row0;
+};
+
 // Kernel shape a plan is made for.
 struct Variant {
   int32_t waves;           // waves per workgroup (32 query rows each)
@@ -39,6 +46,10 @@ constexpr int32_t kMaxQLen = 8;
 constexpr int32_t kMaxHeads = 128;
 constexpr int32_t kMaxRows = 1024;
 constexpr int32_t kMaxSeqLen = 1 << 24;
+// Requests split into at most this many pieces are merged by the short
+// combine kernel, one wave per row and kCombineSmallRows rows per workgroup.
+constexpr int32_t kCombineSmallMax = 16;
+constexpr int32_t kCombineSmallRows = 4;
 
 struct PlanData {
   int32_t batch = 0, q_len = 0, heads = 0, page = 0, num_cus = 0;
@@ -52,6 +63,8 @@ struct PlanData {
   std::vector<Segment> segs;
   std::vector<WorkgroupRange> wgs;  // size grid
   std::vector<CombineJob> jobs;
+  // combine workgroups in launch order (workgroup i runs on XCD i % kNumXcd)
+  std::vector<CombineUnit> cunits;
 };
 
 // Tunables of the planner (exposed for tests; defaults used by the ABI).

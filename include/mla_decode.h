@@ -318,10 +318,12 @@ const char* mla_last_error(void);
  *  MLA_Q_ROWS_PER_BLOCK   query rows (q_len*H flattened) one workgroup holds
  *  MLA_Q_TILE_TOKENS      keys per tile
  *  MLA_Q_NUM_ROW_BLOCKS   row blocks per request
+ *  MLA_Q_NUM_COMBINE_WGS  grid size of the combine kernel (0 when nothing is split)
  * mla_plan_query returns the value (or -1 for an unknown key / NULL plan).
  */
 enum { MLA_Q_NUM_SEGMENTS = 0, MLA_Q_NUM_WORKGROUPS = 1, MLA_Q_NUM_PARTIALS = 2,
-       MLA_Q_ROWS_PER_BLOCK = 3, MLA_Q_TILE_TOKENS = 4, MLA_Q_NUM_ROW_BLOCKS = 5 };
+       MLA_Q_ROWS_PER_BLOCK = 3, MLA_Q_TILE_TOKENS = 4, MLA_Q_NUM_ROW_BLOCKS = 5,
+       MLA_Q_NUM_COMBINE_WGS = 6 };
 int64_t mla_plan_query(const mla_plan* plan, int32_t key);
 
 /* Copy the pieces out: for segment i, seg[4*i + 0..3] = {request, first key,
@@ -329,6 +331,14 @@ int64_t mla_plan_query(const mla_plan* plan, int32_t key);
  * wg[4*w + 0..3] = {first segment, end segment, row block, 0} for workgroup w.
  * Either pointer may be NULL.  Returns MLA_ERR_INVALID_ARGUMENT for a NULL plan. */
 mla_status mla_plan_copy(const mla_plan* plan, int32_t* seg, int32_t* wg);
+
+/* Copy the combine kernel's workgroups out (host only; for tests and tools):
+ * unit[4*i + 0..3] = {request, first partial id, pieces (0 = empty slot),
+ * first query row} for combine workgroup i, which the hardware places on XCD
+ * i % 8.  A workgroup merges 4 rows when no request has more than 16 pieces,
+ * else one.  `unit` holds MLA_Q_NUM_COMBINE_WGS entries of 4 int32 (caller
+ * owned); NULL is allowed.  Returns MLA_ERR_INVALID_ARGUMENT for a NULL plan. */
+mla_status mla_plan_copy_combine(const mla_plan* plan, int32_t* unit);
 
 #ifdef __cplusplus
 }

@@ -41,6 +41,33 @@ def check_plan(lens, q_len, heads, page, num_cus):
     # the busy workgroups fit on the device at once
     busy = int((wg[:, 1] > wg[:, 0]).sum())
     assert busy <= max(nrb, num_cus * (2 if rpb == 64 else 1))
+    # combine workgroups: every row of every split request once, each on the
+    # XCD that wrote most of its partials, at most an even share per XCD
+    cu = p.combine_units()
+    split = np.flatnonzero(pieces > 1)
+    assert (len(cu) == 0) == (len(split) == 0)
+    if len(split):
+        per = 4 if pieces.max() <= 16 else 1
+        rows = q_len * heads
+        first = {b: int(seg[(seg[:, 0] == b) & (seg[:, 3] >= 0), 3].min()) for b in split}
+        seen = np.zeros((len(lens), rows), dtype=np.int32)
+        xcd_of, local, total = {}, 0, 0
+        for s, lst in runs.items():
+            if seg[s, 3] >= 0:
+                for rb, w in lst:
+                    xcd_of[(int(seg[s, 3]), rb)] = w % 8
+        for i, (b, p0, n, r0) in enumerate(cu):
+            if n == 0:
+                continue
+            assert pieces[b] > 1 and n == pieces[b] and p0 == first[b] and r0 % per == 0
+            seen[b, r0:min(r0 + per, rows)] += 1
+            votes = np.bincount([xcd_of[(p0 + k, r0 // rpb)] for k in range(n)], minlength=8)
+            local += int(votes[i % 8] == votes.max())
+            total += 1
+        p.combine_local = local / total
+        assert np.all(seen[split] == 1) and np.all(seen[pieces <= 1] == 0)
+        units = sum(-(-rows // per) for _ in split)
+        assert len(cu) <= 8 * -(-units // 8)
     # workspace size
     slots = p.query(bnd.MLA_Q_NUM_PARTIALS) * nrb
     expect = 0 if slots == 0 else (-(-slots * rpb * 512 * 2 // 256) * 256 + 2 * (-(-slots * rpb * 4 // 256) * 256))
@@ -62,6 +89,9 @@ def test_named_workloads_plan(name):
     if name != "tiny":
         assert used.max() <= 1.2 * used.mean() + 6, (used.max(), used.mean())
         assert len(used) >= 200  # nearly every CU busy
+    if name in ("dsv3", "long"):
+        # each request's pieces sit on one XCD; its combine rows run there too
+        assert p.combine_local == 1.0
 
 
 def test_long_request_is_split_across_the_device():
