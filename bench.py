@@ -11,7 +11,7 @@ larger than 1 GB).
 
 Prints ONE JSON line (value = algorithmic TFLOP/s of the whole step).
 
-    python bench.py [--config dsv3] [--steps 50] [--warmup 10] [--kv bf16|fp8]
+    python bench.py [--config mixed] [--steps 200] [--warmup 20] [--kv bf16|fp8]
 
 With --kv fp8 the same workload runs over an FP8 cache (E4M3 codes with
 per-token E8M0 scales; seeded codes of the same N(0, 1) draw) on the FP8
@@ -127,8 +127,9 @@ def traffic_from(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     kname = "decode_fp8_kernel" if config.endswith("_fp8") else "decode_kernel<"
     fetch = med(_counter_per_dispatch(fetch_dir, "FETCH_SIZE", kname))
     write = med(_counter_per_dispatch(write_dir, "WRITE_SIZE", kname))
-    cfetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "combine_kernel")
-    cwrite = _counter_per_dispatch(write_dir, "WRITE_SIZE", "combine_kernel")
+    # both combine kernels (combine_kernel and combine_small_kernel)
+    cfetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "combine")
+    cwrite = _counter_per_dispatch(write_dir, "WRITE_SIZE", "combine")
     res = {
         "config": config,
         "kernel_sha": kernel_sha("fp8" if config.endswith("_fp8") else "bf16"),
@@ -151,40 +152,78 @@ def traffic_from(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: st
     return 0
 
 
-def cpu_baseline(x, seconds: float) -> dict:
-    """The fp64 oracle on a bounded sample of requests of the same workload."""
+def _oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _oracle_sample(x, arrays, seconds: float) -> tuple:
+    """Runs the fp64 oracle on whole requests (longest first) until `seconds`
+    of wall time are spent; returns (FLOPs done, seconds, requests done)."""
     import numpy as np
 
     from decode_attention_absorbed_amd import accounting as acc
     from oracle import mla_decode_ref
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    cache = x.cache_f64()
-    qn, qp = x.q_nope_f64(), x.q_pe_f64()
-    done, flops, t0 = [], 0, time.perf_counter()
+    cache, qn, qp = arrays
+    done, flops, t0 = 0, 0, time.perf_counter()
     order = np.argsort(-x.seq_lens, kind="stable") if x.batch > 1 else np.arange(1)
-    for b in order:
-        mla_decode_ref(qn[b : b + 1], qp[b : b + 1], cache, x.block_table[b : b + 1], x.seq_lens[b : b + 1], x.softmax_scale)
-        done.append(int(b))
-        flops += acc.flops([int(x.seq_lens[b])], x.heads, x.q_len)
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {
+    # whole passes over the workload repeat until the time is spent (a small
+    # workload takes a fraction of a second per pass)
+    while time.perf_counter() - t0 < seconds:
+        for b in order:
+            mla_decode_ref(qn[b : b + 1], qp[b : b + 1], cache, x.block_table[b : b + 1], x.seq_lens[b : b + 1],
+                           x.softmax_scale)
+            done += 1
+            flops += acc.flops([int(x.seq_lens[b])], x.heads, x.q_len)
+            if time.perf_counter() - t0 >= seconds:
+                break
+    return flops, time.perf_counter() - t0, done
+
+
+def cpu_baseline(x, seconds: float, single_thread_seconds: float = 0.0) -> dict:
+    """The fp64 oracle as it stands, timed on this host on a bounded sample of
+    whole requests of the same workload, with every BLAS thread and (when
+    single_thread_seconds > 0) with one."""
+    arrays = (x.cache_f64(), x.q_nope_f64(), x.q_pe_f64())  # widened once, outside the timed samples
+    flops, dt, done = _oracle_sample(x, arrays, seconds)
+    res = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(_oracle_threads()),
         "kind": "oracle",
-        "sample": f"{len(done)} of {x.batch} requests (fp64 numpy, {dt:.1f} s)",
+        "sample": f"{done} requests of the {x.batch}-request workload, longest first, whole passes repeated "
+                  f"(fp64 numpy, {dt:.1f} s)",
     }
+    if single_thread_seconds > 0:
+        try:
+            from threadpoolctl import threadpool_limits
+
+            with threadpool_limits(limits=1):
+                f1, d1, n1 = _oracle_sample(x, arrays, single_thread_seconds)
+            res["single_thread"] = {"value": f1 / d1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                    "sample": f"{n1} requests, same order ({d1:.1f} s)"}
+        except Exception as e:  # threadpoolctl missing: report why, keep the all-core figure
+            res["single_thread"] = {"error": str(e)}
+    return res
 
 
-def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float, kv: str = "bf16") -> dict:
+def _quantiles(xs: list) -> dict:
+    xs = sorted(xs)
+    q = lambda p: xs[min(len(xs) - 1, int(p * len(xs)))]
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "n": len(xs)}
+
+
+def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf16", diag: int = 100,
+        cpu_single_seconds: float = 0.0) -> dict:
+    """One workload: `steps` decode steps (decode kernel + combine kernel)
+    timed as one region between two HIP events on the launch stream, then
+    diagnostics (`diag` individually timed steps, and bursts of each kernel
+    alone) outside that region."""
     import torch
 
     import decode_attention_absorbed_amd as mla
@@ -201,6 +240,8 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
     t = x.to_torch(dev)
     cache_t = t["cache_codes"] if fp8 else t["cache"]
     kv_bytes = cache_t.numel() * cache_t.element_size()
+    # every step reads its own copy of the cache and queries: the copies
+    # together exceed 1 GB, so repeats are not served by the 256 MB last-level cache
     copies = max(1, min(16, -(-(1 << 30) // max(kv_bytes, 1))))
     caches = [cache_t] + [cache_t.clone() for _ in range(copies - 1)]
     scales = ([t["cache_exps"]] + [t["cache_exps"].clone() for _ in range(copies - 1)]) if fp8 else None
@@ -229,62 +270,64 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
             bnd._check(L.mla_decode_partials(plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(),
                                              int(caches[c].shape[0]), *tail))
 
-    def combine():
-        bnd._check(L.mla_decode_combine(plan.handle, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream))
+    def combine(i=0):
+        bnd._check(L.mla_decode_combine(plan.handle, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), plan.workspace_bytes,
+                                        stream.cuda_stream))
+
+    def step(i):
+        partials(i)
+        combine(i)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def burst(fn, n, offset=0):
+        """n launches back to back between one pair of events: ms per launch."""
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(n):
+            fn(offset + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
 
     for i in range(warmup):
-        partials(i)
-        combine()
+        step(i)
     torch.cuda.synchronize()
 
     # The timed region: exactly `steps` steps between two events, nothing else
-    # on the stream (an event recorded between kernels adds several
-    # microseconds of idle time per step, so the split below is a separate pass).
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # on the stream.
     w0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(steps):
-        partials(i)
-        combine()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    ms_step = burst(step, steps)
     wall = time.perf_counter() - w0
-    ms_step = t0.elapsed_time(t1) / steps
 
-    # Per-kernel split of a step (diagnostic pass with events between the kernels).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        partials(i)
-        ev[i][1].record(stream)
-        combine()
-        ev[i][2].record(stream)
+    # Diagnostics, outside the timed region.
+    # (1) `diag` steps timed one by one (each between its own events), for the spread;
+    per_step = []
+    for i in range(diag):
+        a, b = ev(), ev()
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        per_step.append((a, b))
     torch.cuda.synchronize()
-    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    cmb_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    dec_avg = sum(dec_ms) / steps
-    cmb_avg = sum(cmb_ms) / steps
-    # Kernel duration for the roofline: the same decode launches back to back
-    # between one pair of events on the launch stream (the per-kernel events
-    # above also hold the gap between the previous kernel's end and this start).
-    burst = max(steps, 20)
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for i in range(burst):
-        partials(i)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    dec_burst = b0.elapsed_time(b1) / burst
+    step_q = _quantiles([a.elapsed_time(b) for a, b in per_step])
+    # (2) bursts of each kernel alone (the combine re-reads the last partials).
+    cmb_ms = burst(combine, diag) if plan.workspace_bytes else 0.0
+    dec_burst = burst(partials, diag)
+    # The decode kernel's share of a timed step: the step minus the combine
+    # kernel's launch time.  This never exceeds the step; rocprofv3's kernel
+    # trace of the same build gives the decode duration to compare with.
+    dec_ms = max(ms_step - cmb_ms, 1e-9)
 
     flops = roof["flops"]
     nbytes = roof["bytes"]
     bound = roof["bound"]
     if bound == "hbm":
-        achieved = nbytes / (dec_burst * 1e-3) / 1e9
+        achieved = nbytes / (dec_ms * 1e-3) / 1e9
         peak, unit = acc.PEAK_HBM_BYTES_PER_S / 1e9, "GB/s"
     else:
-        achieved = flops / (dec_burst * 1e-3) / 1e12
+        achieved = flops / (dec_ms * 1e-3) / 1e12
         peak, unit = (acc.PEAK_FP8_FLOPS if fp8 else acc.PEAK_BF16_FLOPS) / 1e12, "TFLOP/s"
     traffic = load_traffic(config, kv)
     res = {
@@ -312,6 +355,7 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
             "kv_tokens": int(sum(lens)),
         },
         "hbm_gbps": nbytes / (ms_step * 1e-3) / 1e9,
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
         "roofline": {
             "bound": bound,
             "achieved": achieved,
@@ -320,27 +364,34 @@ def run(config: str, steps: int, warmup: int, want_cpu: bool, cpu_seconds: float
             "frac": achieved / peak,
             "traffic": traffic,
             "kernel": "decode_fp8_kernel" if fp8 else "decode_kernel",
-            "duration_ms": dec_burst,
+            "duration_ms": dec_ms,
+            "duration_source": "timed step minus the combine kernel's burst time",
         },
         "step_roofline_frac": roof["t_bound"] / (ms_step * 1e-3),
-        "decode_kernel_ms": dec_burst,
-        "decode_kernel_ms_in_step": dec_avg,
-        "decode_kernel_ms_p10_p90": [dec_ms[steps // 10], dec_ms[(9 * steps) // 10]],
-        "combine_kernel_ms": cmb_avg,
+        "step_ms_quantiles": step_q,
+        "decode_kernel_ms": dec_ms,
+        "decode_kernel_burst_ms": dec_burst,
+        "combine_kernel_ms": cmb_ms,
         "plan_ms": plan_ms,
         "wall_ms_per_step": wall * 1e3 / steps,
         "algorithmic_flops": flops,
         "algorithmic_bytes": nbytes,
+        "roofline_ms": roof["t_bound"] * 1e3,
         "input_copies": copies,
         "num_workgroups": plan.query(bnd.MLA_Q_NUM_WORKGROUPS),
         "num_partials": plan.query(bnd.MLA_Q_NUM_PARTIALS),
         "kernel_sha": kernel_sha(kv),
     }
-    if want_cpu:
-        res["cpu_baseline"] = cpu_baseline(x, cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    res["cpu_baseline"] = cpu_baseline(x, cpu_seconds, cpu_single_seconds) if cpu_seconds > 0 else None
+    del caches, qns, qps, scales, t
+    torch.cuda.empty_cache()
     return res
+
+
+#: keys of a workload record that a sub-record repeats (the rest is headline-only)
+SUB_KEYS = ["value", "unit", "ms_per_step", "dtype", "config", "hbm_gbps", "tflops", "roofline", "step_roofline_frac",
+            "step_ms_quantiles", "decode_kernel_ms", "decode_kernel_burst_ms", "combine_kernel_ms", "plan_ms",
+            "roofline_ms", "algorithmic_flops", "algorithmic_bytes", "num_workgroups", "num_partials", "cpu_baseline"]
 
 
 def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
@@ -486,15 +537,19 @@ def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="dsv3", help="tiny | dsv3 | mtp | mixed | long | mtp4 | mtp8")
-    ap.add_argument("--all", action="store_true", help="also run every workload; per-workload lines go to stderr")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mixed", help="headline workload: tiny | dsv3 | mtp | mixed | long | mtp4 | mtp8")
+    ap.add_argument("--subrecords", default="tiny,dsv3,mtp,long,mtp4,mtp8",
+                    help="other workloads measured into the same JSON line (comma list; empty for none)")
+    ap.add_argument("--diag", type=int, default=100, help="individually timed steps and kernel bursts per workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
     ap.add_argument("--layer", action="store_true",
                     help="time prolog + decode + combine + up-projection + output projection per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample of the headline workload (all cores)")
+    ap.add_argument("--cpu-single-seconds", type=float, default=5.0, help="same sample with one BLAS thread")
+    ap.add_argument("--sub-cpu-seconds", type=float, default=2.0, help="oracle sample per sub-record (each thread setting)")
     ap.add_argument("--calibrate-copy", action="store_true", help="run the plain copy the traffic counters are scaled by")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<config>.json from rocprofv3 counter output (no GPU needed)")
@@ -510,12 +565,17 @@ def main() -> int:
     if args.layer:
         print(json.dumps(run_layer(args.config, args.steps, args.warmup, args.kv)), flush=True)
         return 0
-    if args.all:
-        for name in ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"]:
-            r = run(name, args.steps, args.warmup, False, 0.0, args.kv)
-            print(json.dumps(r), file=sys.stderr, flush=True)
-    res = run(args.config, args.steps, args.warmup, not args.no_cpu_baseline and args.kv == "bf16", args.cpu_seconds,
-              args.kv)
+    cpu = not args.no_cpu_baseline and args.kv == "bf16"
+    subs = {}
+    for name in [n for n in args.subrecords.split(",") if n and n != args.config]:
+        r = run(name, max(20, args.steps // 4), args.warmup, args.sub_cpu_seconds if cpu else 0.0, args.kv, args.diag,
+                args.sub_cpu_seconds if cpu else 0.0)
+        subs[name] = {k: r[k] for k in SUB_KEYS}
+        print(f"# {name}: {r['ms_per_step'] * 1e3:.2f} us/step, decode {r['decode_kernel_ms'] * 1e3:.2f} us, "
+              f"roofline frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+    res = run(args.config, args.steps, args.warmup, args.cpu_seconds if cpu else 0.0, args.kv, args.diag,
+              args.cpu_single_seconds if cpu else 0.0)
+    res["configs"] = subs
     print(json.dumps(res), flush=True)
     return 0
 
