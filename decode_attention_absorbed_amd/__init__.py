@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     Plan,
     lib,
     mla_decode,
+    mla_decode_noalloc,
     mla_decode_plan,
     mla_decode_plan_host,
     mla_decode_workspace_bytes,

@@ -56,6 +56,7 @@ EXPORTED = (
     "mla_up_project",
     "mla_o_project_workspace_bytes",
     "mla_o_project",
+    "mla_decode_noalloc",
 )
 
 #: kv_format values of mla_prolog
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
         vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, vp, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     L.mla_decode.restype = ctypes.c_int
+    L.mla_decode_noalloc.argtypes = L.mla_decode.argtypes[:11] + [vp]
+    L.mla_decode_noalloc.restype = ctypes.c_int
     L.mla_decode_partials.argtypes = L.mla_decode.argtypes
     L.mla_decode_partials.restype = ctypes.c_int
     L.mla_decode_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -299,6 +302,39 @@ def mla_decode(
             _ptr(workspace),
             int(ws_bytes),
             stream.cuda_stream,
+        )
+    )
+    return out, lse
+
+
+def mla_decode_noalloc(
+    plan: Plan,
+    q_nope_absorbed: torch.Tensor,
+    q_pe: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    softmax_scale: float,
+    out: torch.Tensor,
+    lse: torch.Tensor,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode without a workspace: the library's per-GPU scratch holds the
+    partials (no allocation in the call; out and lse come from the caller)."""
+    B, qlen, H = plan.batch, plan.q_len, plan.num_heads
+    _expect(q_nope_absorbed, "q_nope_absorbed", torch.bfloat16, (B, qlen, H, 512))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, qlen, H, 64))
+    _expect(kv_cache, "kv_cache", torch.bfloat16, tuple(kv_cache.shape))
+    _expect(block_table, "block_table", torch.int32, tuple(block_table.shape))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+    _expect(out, "out", torch.float32, (B, qlen, H, 512))
+    _expect(lse, "lse", torch.float32, (B, qlen, H))
+    if stream is None:
+        stream = torch.cuda.current_stream(q_nope_absorbed.device)
+    _check(
+        lib().mla_decode_noalloc(
+            plan.handle, _ptr(q_nope_absorbed), _ptr(q_pe), _ptr(kv_cache), int(kv_cache.shape[0]), _ptr(block_table),
+            int(block_table.shape[1]), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse), stream.cuda_stream,
         )
     )
     return out, lse

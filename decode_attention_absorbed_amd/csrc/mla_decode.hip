@@ -47,6 +47,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <utility>
@@ -932,6 +933,16 @@ __global__ __launch_bounds__(64 * kCombineSmallRows) void combine_small_kernel(c
 // C ABI
 // ----------------------------------------------------------------------------
 
+// Device memory of mla_decode_noalloc: the partial outputs of split requests
+// live in this array instead of a caller-provided workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+
 struct mla_plan {
   mla::PlanData d;
   void* dev = nullptr;  // device schedule: segs | wgs | combine units | planned lens
@@ -1061,6 +1072,26 @@ mla_status check_device(const mla_plan* plan) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (device != plan->device)
     return fail(MLA_ERR_INVALID_ARGUMENT, "the current device is not the one the plan was made on");
+  return MLA_OK;
+}
+
+// Device address of `scratch` on `device` (the current device), looked up
+// on the first call for that device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+mla_status scratch_address(int device, void** addr) {
+  if (device < 0 || device >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device id beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[device]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the no-allocation scratch");
+    if (!p) return fail(MLA_ERR_HIP, "hipGetSymbolAddress returned NULL for the no-allocation scratch");
+    g_scratch_addr[device] = p;
+  }
+  *addr = g_scratch_addr[device];
   return MLA_OK;
 }
 
@@ -1307,6 +1338,29 @@ mla_status mla_decode(const mla_plan* plan, const void* q_nope_absorbed, const v
                                      seq_lens, softmax_scale, out, lse, workspace, workspace_bytes, stream);
   if (s != MLA_OK) return s;
   return mla_decode_combine(plan, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_noalloc(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe, const void* kv_cache,
+                              int64_t num_pages, const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                              float softmax_scale, float* out, float* lse, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const size_t need = mla::workspace_bytes(plan->d);
+  if (need > kNoAllocScratchBytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "the plan needs " + std::to_string(need) +
+                                                 " bytes of partials, more than the " +
+                                                 std::to_string(kNoAllocScratchBytes) +
+                                                 "-byte scratch of mla_decode_noalloc (use mla_decode with a workspace)");
+  if (!q_nope_absorbed || !q_pe || !kv_cache || !block_table || !seq_lens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  mla_status st = check_device(plan);
+  if (st != MLA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(plan->device, &ws);
+    if (st != MLA_OK) return st;
+  }
+  return mla_decode(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens, softmax_scale,
+                    out, lse, ws, need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 }  // extern "C"

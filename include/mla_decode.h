@@ -139,6 +139,32 @@ mla_status mla_decode(const mla_plan* plan,
                       void* stream);
 
 /*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device
+ * memory at call time (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and arguments
+ * without the workspace.  The partials of split requests go to a scratch
+ * array the library holds in device memory, 64 MiB per GPU (one copy per
+ * device the library runs on, kept until the process ends; its address is
+ * looked up on the first call on each device).  Allocates nothing and never
+ * synchronizes.
+ *  - A plan whose mla_decode_workspace_bytes exceeds 64 MiB is refused with
+ *    MLA_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ *  - Every call on one GPU shares that GPU's scratch and leaves its contents
+ *    behind: calls that overlap in time on the same GPU (different streams
+ *    without ordering between them) race and give wrong results.  Calls on one
+ *    stream, or otherwise ordered, are safe.  No part of the scratch needs to
+ *    start at zero.
+ * Errors: as for mla_decode (MLA_ERR_INVALID_ARGUMENT, MLA_ERR_WORKSPACE_TOO_SMALL,
+ * MLA_ERR_UNSUPPORTED for device ids beyond 63, MLA_ERR_HIP).
+ */
+mla_status mla_decode_noalloc(const mla_plan* plan,
+                              const void* q_nope_absorbed, const void* q_pe,
+                              const void* kv_cache, int64_t num_pages,
+                              const int32_t* block_table, int32_t bt_stride,
+                              const int32_t* seq_lens, float softmax_scale,
+                              float* out, float* lse, void* stream);
+
+/*
  * The two halves of mla_decode, for callers that want to time, reorder or
  * overlap them.  mla_decode == mla_decode_partials followed by
  * mla_decode_combine on the same stream, with the same plan and workspace.
