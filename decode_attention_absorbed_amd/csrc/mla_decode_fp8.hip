@@ -4,7 +4,8 @@
 // deployment best practices on Ascend servers", section 3.2.1 and section
 // 6.1): every head of a request attends over the same cached rows
 // [c_kv | k_pe]; V is c_kv.  The same report names 8-bit keys and values as
-// the next step for MLA (section 6.1, closing remarks); this kernel takes them
+// future work for MLA (section 8 on next steps, the bullet on quantized MLA
+// operators); this kernel takes them
 // in the OCP FP8 formats that gfx950's matrix cores read natively:
 //  * cache: each token is 576 E4M3 codes plus one E8M0 scale byte e_t
 //    (value 2^(e_t - 127)), so K_t = 2^(e_t - 127) * codes_t and V_t = K_t[0:512];
@@ -400,7 +401,12 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
 
     auto page_at = [&](int pidx) {
       const int rel = pidx - first_pg;
-      return rel < 64 ? __builtin_amdgcn_readlane(pg_lane, rel) : bt_row[pidx];
+      if (rel < 64) return __builtin_amdgcn_readlane(pg_lane, rel);
+      // Further pages: a uniform index read through the constant address
+      // space, so the compiler issues a scalar load (waited for with lgkmcnt)
+      // instead of a vector load whose vmcnt(0) would drain the tile copies.
+      const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt_row;
+      return bt_s[__builtin_amdgcn_readfirstlane(pidx)];
     };
     auto fetch_pages = [&](int tb) {
       TilePages8<NPG> tp;
@@ -410,9 +416,18 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       for (int k = 0; k < NPG; ++k) tp.pg[k] = page_at(min(tp.first + k, last));
       return tp;
     };
+    // A page id outside [0, num_pages) is never followed: page 0 is read
+    // instead, and the piece's rows end as NaN (bad_pg), like a length mismatch.
+    // page ids are int32: a pool of 2^31 pages or more holds every id
+    const uint32_t num_pages_u32 = (uint32_t)min(num_pages, (int64_t)0x80000000LL);
+    bool bad_pg = false;
     auto checked = [&](TilePages8<NPG> tp) {
 #pragma unroll
-      for (int k = 0; k < NPG; ++k) tp.pg[k] = ((uint64_t)(int64_t)tp.pg[k] < (uint64_t)num_pages) ? tp.pg[k] : 0;
+      for (int k = 0; k < NPG; ++k) {
+        const bool ok = (uint32_t)tp.pg[k] < num_pages_u32;  // scalar compare (ids are uniform)
+        bad_pg = bad_pg || !ok;
+        tp.pg[k] = ok ? tp.pg[k] : 0;
+      }
       return tp;
     };
     // Page of token tok (inside the tile of tp).
@@ -423,7 +438,13 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         const int k = (tok >> page_log2) - tp.first;
         int p = tp.pg[0];
 #pragma unroll
-        for (int j = 1; j < NPG; ++j) p = (k == j) ? tp.pg[j] : p;
+        for (int j = 1; j < NPG; ++j) {
+          // the empty asm keeps the (uniform) ids out of an indexed stack
+          // array, which the compiler otherwise builds from this select chain
+          int c = tp.pg[j];
+          asm("" : "+s"(c));
+          p = (k == j) ? c : p;
+        }
         return p;
       }
     };
@@ -762,7 +783,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     o8_drain();
     const float l_tot = pair_sum(l_part);
     float lse_v = l_tot > 0.f ? (mu + __builtin_amdgcn_logf(l_tot)) * kLn2_8 : -INFINITY;
-    if (bad_len) lse_v = NAN;
+    if (bad_len || bad_pg) lse_v = NAN;
     // O holds sum_t p_t 2^(e_t - e0 + 6) codes_t = 2^(133 - e0) sum_t p_t V_t.
     const int oexp = e0 - 127 - kWeightExp8;
     // Every wave is past its last LDS read of the piece (and its copies have
@@ -773,8 +794,13 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     const int nrow = min(32, rows - wave_row0);  // rows of this wave to store
     if (sg.partial < 0) {
       float inv = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, oexp) : 0.f;
-      if (bad_len) inv = NAN;
-      float* obase = out + ((int64_t)b * rows + wave_row0) * 512 + 4 * lane;
+      if (bad_len || bad_pg) inv = NAN;
+      // The lane index goes through an empty asm so that this address is
+      // formed here and not hoisted above the tile loop, where it would hold
+      // a register pair for the whole piece.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      float* obase = out + ((int64_t)b * rows + wave_row0) * 512 + 4 * ln;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h == 0)
@@ -786,23 +812,31 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
           store_wt(obase + (int64_t)r * 512 + 256 * h, v);
         }
       }
-      if (row_ok && g == 0) lse[(int64_t)b * rows + row] = lse_v;
+      if (row_ok && g == 0) {
+        int r = row;  // formed here, not hoisted above the tile loop
+        asm volatile("" : "+v"(r));
+        lse[(int64_t)b * rows + r] = lse_v;
+      }
     } else {
       const int64_t slot = (int64_t)sg.partial * nrb + rb;
       float amax = pair_max(o8_absmax_rec<0>(0.f));
       const int e = max(__builtin_amdgcn_frexp_expf(amax), -110);
       const float c = __builtin_ldexpf(1.f, 15 - e);
       float f = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, e - 15 + oexp) : 0.f;
-      if (bad_len) f = NAN;
+      if (bad_len || bad_pg) f = NAN;
       o8_stage_half_rec<0>(stg_row, c);
       typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-      _Float16* hbase = reinterpret_cast<_Float16*>(ws_o) + (slot * kRowsPerBlock8 + wave * 32) * 512 + 8 * lane;
+      int ln = lane;  // formed here, not hoisted above the tile loop (see above)
+      asm volatile("" : "+v"(ln));
+      _Float16* hbase = reinterpret_cast<_Float16*>(ws_o) + (slot * kRowsPerBlock8 + wave * 32) * 512 + 8 * ln;
       for (int r = 0; r < nrow; ++r) {
         const f16x8 v = *LDS_AS(const f16x8, (uintptr_t)(stg + r * kStageRow8 + 16 * lane));
         store_wt(hbase + (int64_t)r * 512, v);
       }
       if (row_ok && g == 0) {
-        const int64_t ri = slot * kRowsPerBlock8 + row_local;
+        int rl = row_local;  // formed here, not hoisted above the tile loop
+        asm volatile("" : "+v"(rl));
+        const int64_t ri = slot * kRowsPerBlock8 + rl;
         ws_lse[ri] = lse_v;
         ws_f[ri] = f;
       }

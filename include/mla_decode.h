@@ -105,8 +105,10 @@ size_t mla_decode_workspace_bytes(const mla_plan* plan);
  *  q_pe             device bf16 [B, q_len, H, 64]; 16-byte aligned; post-RoPE.
  *  kv_cache         device bf16 [num_pages, page_size, 576]; 16-byte aligned.
  *                   Row = [c_kv (512) | k_pe (64)]; V is the c_kv part.
- *  num_pages        pages in kv_cache (> 0).  Page ids outside [0, num_pages)
- *                   read page 0 instead of faulting (results are then garbage).
+ *  num_pages        pages in kv_cache (> 0).  A page id outside [0, num_pages)
+ *                   is never followed: the request whose block-table entry it
+ *                   is gets NaN in all of its out and lse (loud, no fault);
+ *                   other requests are unaffected.
  *  block_table      device int32 [B, bt_stride]: token t of request b lives in
  *                   slot t % page_size of page block_table[b, t / page_size].
  *                   Entries past ceil(seq_lens[b] / page_size) are never read;
@@ -193,8 +195,9 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse,
  * FP8 latent cache.
  *
  * The Huawei report ("DeepSeek V3/R1 inference deployment best practices on
- * Ascend servers", section 6.1) names 8-bit keys and values as the next step
- * for MLA decode; these entry points take the cache in the OCP FP8 formats
+ * Ascend servers", section 8 on next steps, the bullet on quantized MLA
+ * operators) names 8-bit keys and values as future work for MLA decode; these
+ * entry points take the cache in the OCP FP8 formats
  * that gfx950's matrix cores read.  Same computation and output as
  * mla_decode, except:
  *

@@ -27,6 +27,7 @@ from .mla_oracle import (  # noqa: F401
 from .mla_oracle_fp8 import (  # noqa: F401
     E4M3_MAX,
     E4M3_REL_RMS,
+    E4M3_REL_RMS_AVG,
     dequantize_cache,
     dequantize_query,
     e4m3_decode,

@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY: see the package docstring.
 
 The pages describe the computation in bf16 and name 8-bit keys and values as
 future work (Huawei, "DeepSeek V3/R1 inference deployment best practices on
-Ascend servers", section 6.1, the closing remarks on INT8 KV and fully INT8
-MLA; the same report notes in section 3.1.1 that the Ascend parts lack FP8).
+Ascend servers", section 8 on next steps, the bullet on INT8 KV and fully
+INT8 MLA operators; the digest of "Serving LLMs on Huawei CloudMatrix384"
+notes, in its description of the Ascend 910 die, that the part has no FP8).
 This module fixes the FP8 variant the HIP library implements; every choice
 below is a reading, listed with the others in the design notes:
 
@@ -192,10 +193,16 @@ def mla_decode_fp8_ref(
     return out, lse
 
 
-#: E4M3 keeps 3 mantissa bits: rounding to nearest changes a normal value by at
-#: most 2^-4 of itself, and a rounding error spread evenly over that interval
-#: has a root mean square of 2^-4 / sqrt(3).
+#: E4M3 keeps 3 mantissa bits: a normal value x = 2^(k + phi) (0 <= phi < 1)
+#: lies on a grid of step 2^(k - 3), so rounding to nearest changes it by at
+#: most half a step, 2^(-4 - phi) of itself.  An error spread evenly over
+#: +-half a step has a root mean square of step / sqrt(12); relative to x that
+#: is 2^(-3 - phi) / sqrt(12), largest (2^-4 / sqrt(3)) at the bottom of a binade:
 E4M3_REL_RMS = 2.0 ** -4 / math.sqrt(3.0)
+#: and, averaged over where x falls inside its binade (phi uniform, as for the
+#: kernel's scaled weights, whose log2 has no preferred fractional part), the
+#: root of the mean of 2^(-6 - 2 phi) / 12 = 2^-3 / sqrt(12) * sqrt(3 / (8 ln 2)).
+E4M3_REL_RMS_AVG = 2.0 ** -3 / math.sqrt(12.0) * math.sqrt(3.0 / (8.0 * math.log(2.0)))
 
 
 def fp8_weight_error_rms(
@@ -215,11 +222,15 @@ def fp8_weight_error_rms(
         a_t = w_t / w_max * 2^weight_exp * 2^(e_t - e_max)
     (the row's largest weight lands at 2^weight_exp for a token with the
     largest scale exponent e_max of the request).  A normal a_t (>= 2^-6) is
-    rounded with independent relative error of rms E4M3_REL_RMS; a subnormal
-    one with absolute error of rms min(2^-10 / sqrt(3), a_t) (the subnormal
-    step is 2^-9; values below half a step round to zero).  Back in weight
-    units the error is err_t = that / (a_t / w_t), and the output error of
-    element d is sqrt(sum_t err_t^2 V_td^2).
+    rounded with independent relative error of rms E4M3_REL_RMS_AVG (the
+    uniform-rounding-noise rms of the E4M3 grid averaged over the position
+    inside the binade: the kernel puts each tile's largest weight at a
+    position inside [2^6, 2^7) set by the scores, not at the binade's
+    bottom); a subnormal one with absolute error of rms
+    min(2^-10 / sqrt(3), a_t) (the subnormal step is 2^-9; values below half
+    a step round to zero).  Back in weight units the error is
+    err_t = that / (a_t / w_t), and the output error of element d is
+    sqrt(sum_t err_t^2 V_td^2).
     """
     codes, f = quantize_query(q_nope, q_pe)
     q = dequantize_query(codes, f)
@@ -244,7 +255,7 @@ def fp8_weight_error_rms(
             w = np.exp(s - s.max(axis=-1, keepdims=True))
             w /= w.sum(axis=-1, keepdims=True)
             a = w / w.max(axis=-1, keepdims=True) * gain
-            err_a = np.where(a >= 2.0**-6, E4M3_REL_RMS * a, np.minimum(2.0**-10 / math.sqrt(3.0), a))
+            err_a = np.where(a >= 2.0**-6, E4M3_REL_RMS_AVG * a, np.minimum(2.0**-10 / math.sqrt(3.0), a))
             err = err_a * (w / np.where(a > 0, a, 1.0))
             rms[b, j] = np.sqrt((err**2) @ (K[:, :D_LATENT] ** 2))
     return rms

@@ -194,3 +194,66 @@ def pending_load_violations(body: list) -> list:
         if any(_regs(o) & live for o in ops):
             bad.append(t)
     return bad
+
+
+def _function_lines(asm: str, prefix: str) -> list:
+    """Raw lines (comments kept) of every function whose symbol starts with prefix."""
+    lines = asm.split("\n")
+    out = []
+    for i, l in enumerate(lines):
+        if l.startswith(prefix) and l.split(";")[0].rstrip().endswith(":"):
+            body = []
+            for t in lines[i + 1 :]:
+                if ".Lfunc_end" in t:
+                    break
+                body.append(t)
+            out.append(body)
+    return out
+
+
+def compiler_agpr_uses(asm: str, prefix: str) -> list:
+    """Instructions outside inline-asm blocks (;;#ASMSTART .. ;;#ASMEND) that
+    name an accumulation register.  The decode kernels keep their output
+    accumulators in AGPRs that only their inline asm touches; an instruction
+    the compiler generated itself that reads or writes an a-register would
+    mean the allocator placed something there (clobber lists do not reserve
+    registers between asm statements)."""
+    bad = []
+    for body in _function_lines(asm, prefix):
+        inside = False
+        for l in body:
+            s = l.strip()
+            if s.startswith(";;#ASMSTART"):
+                inside = True
+                continue
+            if s.startswith(";;#ASMEND"):
+                inside = False
+                continue
+            t = s.split(";")[0].strip()
+            if inside or not t or t.startswith(".") or t.endswith(":"):
+                continue
+            op, ops = _split(t)
+            if op and any(re.match(r"a(\d+|\[\d+:\d+\])$", o) for o in ops):
+                bad.append(t)
+    return bad
+
+
+def kernel_resources(asm: str) -> dict:
+    """Per kernel symbol: spilled VGPRs/SGPRs and private (scratch) bytes, from
+    the code object metadata."""
+    res = {}
+    cur = None
+    for l in asm.split("\n"):
+        s = l.strip()
+        m = re.match(r"\.name:\s+(\S+)", s)
+        if m:
+            cur = m.group(1)
+            res.setdefault(cur, {})
+            continue
+        if cur is None:
+            continue
+        for key in ("vgpr_spill_count", "sgpr_spill_count", "private_segment_fixed_size"):
+            m = re.match(r"\." + key + r":\s+(\d+)", s)
+            if m:
+                res[cur][key] = int(m.group(1))
+    return res

@@ -61,6 +61,35 @@ def test_only_explicit_vmcnt_waits(asm):
         assert counts == [0, 9, 18, 36], waits
 
 
+def test_accumulators_only_touched_by_inline_asm(asm):
+    # the 256 output accumulators live in a0..a255, named only by inline asm
+    assert asm_checks.compiler_agpr_uses(asm, asm_checks.DECODE_PREFIX) == []
+
+
+def test_decode_kernels_do_not_spill(asm):
+    res = {k: v for k, v in asm_checks.kernel_resources(asm).items() if k.startswith(asm_checks.DECODE_PREFIX)}
+    assert len(res) == 2
+    for name, r in res.items():
+        # no VGPR spills and no scratch memory at all (spilled SGPRs go to
+        # lanes of a VGPR, not to memory)
+        assert r.get("vgpr_spill_count") == 0, (name, r)
+        assert r.get("private_segment_fixed_size") == 0, (name, r)
+
+
+def test_every_load_result_waited_for(asm):
+    # in-order vmcnt model: no register of an outstanding load is touched
+    for body in asm_checks.kernel_bodies(asm):
+        assert asm_checks.pending_load_violations(body) == []
+
+
+def test_page_ids_not_loaded_by_vector_loads(asm):
+    # one vector dword load (the piece's first 64 page ids, waited for
+    # explicitly); pages further on come from scalar loads, never from a vector
+    # load whose wait would drain the tile copies
+    for body in asm_checks.kernel_bodies(asm):
+        assert sum(t.startswith("global_load_dword ") for t in body) == 1
+
+
 def test_no_store_data_hazards(asm):
     # every kernel of the library: the decode kernel's inline-asm stores and
     # the compiler's own stores in the combine kernels
@@ -113,6 +142,39 @@ def test_fp8_async_query_loads_untouched_until_waited(asm_fp8):
     for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
         assert sum(t.startswith("global_load_dwordx4") for t in body) == 36
         assert asm_checks.async_load_violations(body) == []
+
+
+def test_fp8_only_explicit_vmcnt_waits(asm_fp8):
+    # the counts the FP8 kernel's source writes: 24/22/20 (prologue, query and
+    # scale copies in flight), 10 (one tile of copies in flight), 0 (drain)
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
+        waits = asm_checks.vmcnt_waits(body)
+        counts = sorted({int(w.split("vmcnt(")[1].split(")")[0]) for w in waits})
+        assert counts == [0, 10, 20, 22, 24], waits
+
+
+def test_fp8_every_load_result_waited_for(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
+        assert asm_checks.pending_load_violations(body) == []
+
+
+def test_fp8_page_ids_not_loaded_by_vector_loads(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
+        assert sum(t.startswith("global_load_dword ") for t in body) == 1
+
+
+def test_fp8_accumulators_only_touched_by_inline_asm(asm_fp8):
+    assert asm_checks.compiler_agpr_uses(asm_fp8, FP8_PREFIX) == []
+
+
+def test_fp8_kernels_do_not_spill(asm_fp8):
+    res = {k: v for k, v in asm_checks.kernel_resources(asm_fp8).items() if k.startswith(FP8_PREFIX)}
+    assert len(res) == 3
+    for name, r in res.items():
+        # no VGPR spills and no scratch memory at all (spilled SGPRs go to
+        # lanes of a VGPR, not to memory)
+        assert r.get("vgpr_spill_count") == 0, (name, r)
+        assert r.get("private_segment_fixed_size") == 0, (name, r)
 
 
 # ---- the prolog / epilog projections -----------------------------------------------------

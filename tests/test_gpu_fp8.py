@@ -6,9 +6,10 @@ so lse differs only by fp32 rounding (bar: max-abs <= 1e-3, as for bf16, or the
 worst-case rounding of a 576-term fp32 sum where scores are large).  The
 output differs mainly because the kernel rounds the softmax weights to E4M3
 before the PV product; ``fp8_weight_error_rms`` gives the root-mean-square
-size of that error per element.  Bars: the L2 norm of the error is at most
-2x the model's, and every element is within 8 model standard deviations
-(+ 1e-4 for fp32 rounding).
+size of that error per element (pinned against a direct simulation of the
+rounding to within 0.75-1.33x).  Bars: the L2 norm of the error is at most
+1.25x the model's, every element is within 6 model standard deviations
+(+ 1e-4 for fp32 rounding), and the relative L2 error is at most 3%.
 """
 import math
 
@@ -36,7 +37,7 @@ from workloads import (  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 LSE_MAX_ABS = 1e-3
-RMS_FACTOR, SIGMAS, ABS_FLOOR = 2.0, 8.0, 1e-4
+RMS_FACTOR, SIGMAS, ABS_FLOOR, REL_L2_CAP = 1.25, 6.0, 1e-4, 0.03
 
 
 @pytest.fixture(scope="module")
@@ -101,6 +102,7 @@ def compare(out, lse, ref_o, ref_l, rms, s_abs, what=""):
     assert np.all(np.abs(lse - ref_l) <= bar_l), f"{what}: lse max-abs {e_l}"
     assert ratio <= RMS_FACTOR, f"{what}: error L2 is {ratio:.2f}x the model's"
     assert worst <= 1.0, f"{what}: an element is {worst:.2f}x past its bar"
+    assert rel <= REL_L2_CAP, f"{what}: relative L2 error {rel:.3f}"
 
 
 SMALL = [
@@ -133,24 +135,46 @@ def test_fp8_forced_split_counts(dev, num_cus):
     compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
 
 
-SAMPLES = {"tiny": None, "dsv3": [0, 31], "mtp": "extremes", "mixed": "mixed", "long": None,
-           "mtp4": "extremes", "mtp8": "extremes"}
-
-
 @pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"])
 def test_fp8_named_workload_parity(dev, name):
     x = make_config_fp8(name)
     print(f"{name}: B={x.batch} H={x.heads} q_len={x.q_len} pages={x.num_pages}", flush=True)
     out, lse = run_gpu(x, dev)
-    s = SAMPLES[name]
-    if s == "extremes":
-        idx = [int(np.argmin(x.seq_lens)), int(np.argmax(x.seq_lens))]
-    elif s == "mixed":
-        idx = list(np.flatnonzero(x.seq_lens == 20480)[:1]) + list(np.flatnonzero(x.seq_lens == 400)[:2])
-    else:
-        idx = list(range(x.batch)) if s is None else s
-    compare(out[idx], lse[idx], *oracle(x, idx), what=f"{name} requests {idx}")
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    compare(out, lse, *oracle(x), what=f"{name}, all {x.batch} requests")
+
+
+@pytest.mark.parametrize("num_cus", [1, 3])
+def test_fp8_pieces_spanning_more_than_64_pages(dev, num_cus):
+    # page 16: a piece of more than 1024 keys reads page ids past the 64 the
+    # kernel keeps in a register (scalar loads from the block table)
+    x = make_inputs_fp8(2, 128, 1, 16, [3000, 2100], seed=38)
+    plan = bnd.mla_decode_fp8_plan(x.seq_lens, x.q_len, x.heads, x.page, num_cus)
+    segs = plan.segments()
+    assert max(-(-int(e) // 16) - int(s) // 16 for _, s, e, _ in segs) > 64
+    out, lse = run_gpu(x, dev, plan=plan)
+    compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
+
+
+@pytest.mark.parametrize("page,lens", [(512, [5000, 700, 513]), (4096, [9000, 4097, 1])], ids=["P512", "P4096"])
+def test_fp8_large_page_sizes(dev, page, lens):
+    x = make_inputs_fp8(len(lens), 128, 1, page, lens, seed=39 + page)
+    out, lse = run_gpu(x, dev)
+    compare(out, lse, *oracle(x), what=f"page {page}")
+
+
+@pytest.mark.parametrize("num_cus", [1, 256])
+def test_fp8_out_of_range_page_ids_give_nan_in_exactly_their_requests(dev, num_cus):
+    x = make_inputs_fp8(3, 128, 2, 16, [400, 200, 333], seed=36)
+    good_o, good_l = run_gpu(x, dev, num_cus=num_cus)
+    bt = x.block_table.copy()
+    # (make_inputs shuffles the requests: index the pages request 0 really has)
+    bt[0, (int(x.seq_lens[0]) - 1) // x.page // 2] = x.num_pages + 7  # past the pool
+    bt[2, 0] = -3
+    out, lse = run_gpu(x, dev, num_cus=num_cus, block_table=torch.from_numpy(bt).to(dev))
+    for b in (0, 2):
+        assert np.all(np.isnan(out[b])) and np.all(np.isnan(lse[b]))
+    np.testing.assert_array_equal(out[1], good_o[1])
+    np.testing.assert_array_equal(lse[1], good_l[1])
 
 
 def test_fp8_page_permutation_is_bitwise_invariant(dev):

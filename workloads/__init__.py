@@ -14,8 +14,9 @@ Workload shapes come from the pages:
   KV cache).
 * One MTP draft token, i.e. two query tokens per request (same report,
   section 5.3 and the x2 factor in section 7.2); 3 and 7 draft tokens for
-  the longer-draft workloads (the CloudMatrix384 digest's serving setup
-  speculates several tokens ahead).
+  the longer-draft workloads (the digest of the LMSYS post on serving
+  DeepSeek-V4-Pro on H20 runs 7 draft tokens; the CloudMatrix384 digest
+  speculates a single token).
 * A mixed batch of 20K-token (40%) and 400-token (60%) requests (Ascend
   troubleshooting note on decode TPOT jitter, section 5.2, the random mixed
   data set).
