@@ -219,11 +219,12 @@ def _quantiles(xs: list) -> dict:
 
 
 def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf16", diag: int = 100,
-        cpu_single_seconds: float = 0.0) -> dict:
+        cpu_single_seconds: float = 0.0, rescale: str = "lazy") -> dict:
     """One workload: `steps` decode steps (decode kernel + combine kernel)
     timed as one region between two HIP events on the launch stream, then
     diagnostics (`diag` individually timed steps, and bursts of each kernel
-    alone) outside that region."""
+    alone) outside that region.  rescale = "pow2" runs the bf16 decode's
+    power-of-two rescale form (mla_decode_variant) instead of mla_decode's."""
     import torch
 
     import decode_attention_absorbed_amd as mla
@@ -258,6 +259,17 @@ def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf1
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     L = mla.lib()
     stream = torch.cuda.current_stream(dev)
+    variant = bnd.MLA_RESCALE_POW2 if rescale == "pow2" else bnd.MLA_RESCALE_LAZY
+    if fp8 and variant != bnd.MLA_RESCALE_LAZY:
+        raise ValueError("the power-of-two rescale form is a bf16 decode variant")
+
+    def decode_variant(i, events_ptr=None):
+        """decode + combine through mla_decode_variant"""
+        c = i % copies
+        bnd._check(L.mla_decode_variant(plan.handle, qns[c].data_ptr(), qps[c].data_ptr(), caches[c].data_ptr(),
+                                        int(caches[c].shape[0]), bt.data_ptr(), int(bt.shape[1]), sl.data_ptr(),
+                                        float(x.softmax_scale), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                        plan.workspace_bytes, variant, events_ptr, stream.cuda_stream))
 
     def partials(i):
         c = i % copies
@@ -275,6 +287,9 @@ def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf1
                                         stream.cuda_stream))
 
     def step(i):
+        if variant != bnd.MLA_RESCALE_LAZY:
+            decode_variant(i)
+            return
         partials(i)
         combine(i)
 
@@ -314,7 +329,20 @@ def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf1
     step_q = _quantiles([a.elapsed_time(b) for a, b in per_step])
     # (2) bursts of each kernel alone (the combine re-reads the last partials).
     cmb_ms = burst(combine, diag) if plan.workspace_bytes else 0.0
-    dec_burst = burst(partials, diag)
+    dec_burst = burst(partials, diag) if variant == bnd.MLA_RESCALE_LAZY else None
+    # (3) how often the online softmax rescaled O: one untimed call with the
+    # rescale counter, against the (wave, tile) pairs the plan runs.
+    rescale_rec = None
+    if not fp8:
+        events = torch.zeros(1, dtype=torch.int32, device=dev)
+        decode_variant(0, events.data_ptr())
+        torch.cuda.synchronize()
+        seg = plan.segments()
+        nrb = plan.query(bnd.MLA_Q_NUM_ROW_BLOCKS)
+        wave_tiles = int(sum(-(-(int(e) - int(s0)) // 32) for s0, e in zip(seg[:, 1], seg[:, 2]))) * 4 * nrb
+        ev_n = int(events.item())
+        rescale_rec = {"form": rescale, "events": ev_n, "wave_tiles": wave_tiles,
+                       "per_1000_wave_tiles": 1000.0 * ev_n / max(wave_tiles, 1)}
     # The decode kernel's share of a timed step: the step minus the combine
     # kernel's launch time.  This never exceeds the step; rocprofv3's kernel
     # trace of the same build gives the decode duration to compare with.
@@ -380,6 +408,7 @@ def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf1
         "input_copies": copies,
         "num_workgroups": plan.query(bnd.MLA_Q_NUM_WORKGROUPS),
         "num_partials": plan.query(bnd.MLA_Q_NUM_PARTIALS),
+        "rescale": rescale_rec,
         "kernel_sha": kernel_sha(kv),
     }
     res["cpu_baseline"] = cpu_baseline(x, cpu_seconds, cpu_single_seconds) if cpu_seconds > 0 else None
@@ -391,7 +420,8 @@ def run(config: str, steps: int, warmup: int, cpu_seconds: float, kv: str = "bf1
 #: keys of a workload record that a sub-record repeats (the rest is headline-only)
 SUB_KEYS = ["value", "unit", "ms_per_step", "dtype", "config", "hbm_gbps", "tflops", "roofline", "step_roofline_frac",
             "step_ms_quantiles", "decode_kernel_ms", "decode_kernel_burst_ms", "combine_kernel_ms", "plan_ms",
-            "roofline_ms", "algorithmic_flops", "algorithmic_bytes", "num_workgroups", "num_partials", "cpu_baseline"]
+            "roofline_ms", "algorithmic_flops", "algorithmic_bytes", "num_workgroups", "num_partials", "rescale",
+            "cpu_baseline"]
 
 
 def run_layer(config: str, steps: int, warmup: int, kv: str = "bf16") -> dict:
@@ -546,6 +576,8 @@ def main() -> int:
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="cache format (bf16: the headline; fp8: E4M3 + E8M0)")
     ap.add_argument("--layer", action="store_true",
                     help="time prolog + decode + combine + up-projection + output projection per step")
+    ap.add_argument("--rescale", default="lazy", choices=["lazy", "pow2"],
+                    help="bf16 O-rescale form: lazy (mla_decode) or pow2 (the power-of-two variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample of the headline workload (all cores)")
     ap.add_argument("--cpu-single-seconds", type=float, default=5.0, help="same sample with one BLAS thread")
@@ -569,12 +601,12 @@ def main() -> int:
     subs = {}
     for name in [n for n in args.subrecords.split(",") if n and n != args.config]:
         r = run(name, max(20, args.steps // 4), args.warmup, args.sub_cpu_seconds if cpu else 0.0, args.kv, args.diag,
-                args.sub_cpu_seconds if cpu else 0.0)
+                args.sub_cpu_seconds if cpu else 0.0, args.rescale)
         subs[name] = {k: r[k] for k in SUB_KEYS}
         print(f"# {name}: {r['ms_per_step'] * 1e3:.2f} us/step, decode {r['decode_kernel_ms'] * 1e3:.2f} us, "
               f"roofline frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
     res = run(args.config, args.steps, args.warmup, args.cpu_seconds if cpu else 0.0, args.kv, args.diag,
-              args.cpu_single_seconds if cpu else 0.0)
+              args.cpu_single_seconds if cpu else 0.0, args.rescale)
     res["configs"] = subs
     print(json.dumps(res), flush=True)
     return 0

@@ -12,6 +12,9 @@ from .binding import (  # noqa: F401
     lib,
     mla_decode,
     mla_decode_noalloc,
+    mla_decode_variant,
+    MLA_RESCALE_LAZY,
+    MLA_RESCALE_POW2,
     mla_decode_plan,
     mla_decode_plan_host,
     mla_decode_workspace_bytes,

@@ -57,7 +57,12 @@ EXPORTED = (
     "mla_o_project_workspace_bytes",
     "mla_o_project",
     "mla_decode_noalloc",
+    "mla_decode_variant",
 )
+
+#: values of mla_decode_variant's `variant` (include/mla_decode.h)
+MLA_RESCALE_LAZY = 0
+MLA_RESCALE_POW2 = 1
 
 #: kv_format values of mla_prolog
 MLA_KV_BF16 = 0
@@ -102,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_noalloc.restype = ctypes.c_int
     L.mla_decode_partials.argtypes = L.mla_decode.argtypes
     L.mla_decode_partials.restype = ctypes.c_int
+    L.mla_decode_variant.argtypes = L.mla_decode.argtypes[:13] + [ctypes.c_int32, vp, vp]
+    L.mla_decode_variant.restype = ctypes.c_int
     L.mla_decode_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.mla_decode_combine.restype = ctypes.c_int
     L.mla_decode_plan_destroy.argtypes = [vp]
@@ -249,20 +256,10 @@ def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ..
         raise ValueError(f"{name} must be on the GPU")
 
 
-def mla_decode(
-    plan: Plan,
-    q_nope_absorbed: torch.Tensor,
-    q_pe: torch.Tensor,
-    kv_cache: torch.Tensor,
-    block_table: torch.Tensor,
-    seq_lens: torch.Tensor,
-    softmax_scale: float,
-    out: Optional[torch.Tensor] = None,
-    lse: Optional[torch.Tensor] = None,
-    workspace: Optional[torch.Tensor] = None,
-    stream: Optional[torch.cuda.Stream] = None,
-) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Enqueue the decode on `stream` (default: the current stream); returns (out, lse)."""
+def _decode_args(plan, q_nope_absorbed, q_pe, kv_cache, block_table, seq_lens, softmax_scale, out, lse, workspace,
+                 stream):
+    """Checks the tensors, allocates out/lse/workspace where not given, and
+    returns (mla_decode's argument list, out, lse)."""
     B, qlen, H = plan.batch, plan.q_len, plan.num_heads
     dev = q_nope_absorbed.device
     _expect(q_nope_absorbed, "q_nope_absorbed", torch.bfloat16, (B, qlen, H, 512))
@@ -286,24 +283,67 @@ def mla_decode(
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    _check(
-        lib().mla_decode(
-            plan.handle,
-            _ptr(q_nope_absorbed),
-            _ptr(q_pe),
-            _ptr(kv_cache),
-            int(kv_cache.shape[0]),
-            _ptr(block_table),
-            int(block_table.shape[1]),
-            _ptr(seq_lens),
-            float(softmax_scale),
-            _ptr(out),
-            _ptr(lse),
-            _ptr(workspace),
-            int(ws_bytes),
-            stream.cuda_stream,
-        )
-    )
+    args = [
+        plan.handle,
+        _ptr(q_nope_absorbed),
+        _ptr(q_pe),
+        _ptr(kv_cache),
+        int(kv_cache.shape[0]),
+        _ptr(block_table),
+        int(block_table.shape[1]),
+        _ptr(seq_lens),
+        float(softmax_scale),
+        _ptr(out),
+        _ptr(lse),
+        _ptr(workspace),
+        int(ws_bytes),
+    ]
+    return args, stream.cuda_stream, out, lse
+
+
+def mla_decode(
+    plan: Plan,
+    q_nope_absorbed: torch.Tensor,
+    q_pe: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    softmax_scale: float,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue the decode on `stream` (default: the current stream); returns (out, lse)."""
+    args, st, out, lse = _decode_args(plan, q_nope_absorbed, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
+                                      out, lse, workspace, stream)
+    _check(lib().mla_decode(*args, st))
+    return out, lse
+
+
+def mla_decode_variant(
+    plan: Plan,
+    q_nope_absorbed: torch.Tensor,
+    q_pe: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    softmax_scale: float,
+    variant: int = MLA_RESCALE_LAZY,
+    rescale_events: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode with the O-rescale form `variant` (MLA_RESCALE_LAZY or
+    MLA_RESCALE_POW2); `rescale_events` (a 1-element int32 device tensor the
+    caller zeroes, or None) is incremented once per (wave, tile) rescale of O."""
+    if rescale_events is not None:
+        _expect(rescale_events, "rescale_events", torch.int32, (1,))
+    args, st, out, lse = _decode_args(plan, q_nope_absorbed, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
+                                      out, lse, workspace, stream)
+    _check(lib().mla_decode_variant(*args, int(variant), _ptr(rescale_events), st))
     return out, lse
 
 

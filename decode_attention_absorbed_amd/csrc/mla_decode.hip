@@ -50,19 +50,13 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <type_traits>
 #include <utility>
 
 #include "decode_fp8.h"
 #include "mla_decode.h"
 #include "plan_internal.h"
 #include "abi_common.h"
-
-// Which bf16 decode kernel the launcher uses: 0 = decode_kernel (4 waves, 32
-// rows each), 1 = decode_pp_kernel (8 waves of 16 rows, two groups half a tile
-// apart).
-#ifndef MLA_PP
-#define MLA_PP 0
-#endif
 
 namespace mla {
 namespace {
@@ -133,10 +127,6 @@ __device__ __forceinline__ void s_mfma_drain(f32x4 (&acc)[4]) {
   asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
 }
 
-__device__ __forceinline__ void s_mfma_drain2(f32x4 (&acc)[2]) {
-  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
-}
-
 // The output accumulators O^T (64 blocks of 16x16 fp32 = 256 registers per
 // lane) live in the physical AGPRs a[0:255]: block n = 2 * cb + hb (columns
 // 16cb .. 16cb+15, row block hb) is a[4n : 4n+3].  Lane l of block n holds
@@ -176,6 +166,17 @@ __device__ __forceinline__ void o_scale_rec(float alpha0, float alpha1) {
 }
 
 __device__ __forceinline__ void o_scale_all(float alpha0, float alpha1) { o_scale_rec<0>(alpha0, alpha1); }
+
+// Power-of-two form of the same update: O <- O * 2^e0 (row block 0) and
+// O * 2^e1 (row block 1), exact, by v_ldexp_f32 (an add to the exponent that
+// also handles zeros, subnormals and underflow).
+template <int R>
+__device__ __forceinline__ void o_ldexp_rec(int e0, int e1) {
+  if constexpr (R < 256) {
+    o_set<R>(__builtin_ldexpf(o_get<R>(), ((R >> 2) & 1) ? e1 : e0));
+    o_ldexp_rec<R + 1>(e0, e1);
+  }
+}
 
 // Wait out the MFMA write -> AGPR read latency before reading results.
 __device__ __forceinline__ void o_drain() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
@@ -232,7 +233,11 @@ struct TilePages {
   int pg[2];
 };
 
-template <bool SINGLE_PAGE>
+// POW2 selects the power-of-two form of the online softmax's reference (the
+// running maximum rounded up to an integer in log2 units, so that O is
+// rescaled by exact powers of two); rescale_events (may be NULL) counts, per
+// wave, the tiles after which O was rescaled.
+template <bool SINGLE_PAGE, bool POW2>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint8_t* __restrict__ cache, int64_t num_pages,
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const Segment* __restrict__ segs, const WorkgroupRange* __restrict__ wgs,
     float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
     float* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
-    float* __restrict__ ws_lse, float* __restrict__ ws_f) {
+    float* __restrict__ ws_lse, float* __restrict__ ws_f, uint32_t* __restrict__ rescale_events) {
   // 4 tile stages (144 KB) + the rope part of the query rows (16 KB): the
   // 160 KB of LDS a workgroup may hold.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kWaves * kQpeWaveBytes];
@@ -270,6 +275,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
   // The wave's first row has the fewest visible keys; a wave with rows past
   // the end masks every tile.
   const int wave_row0 = rb * kRowsPerBlock + wave * 32;
+  uint32_t n_rescale = 0;  // tiles after which this wave rescaled O (uniform)
   const bool wave_full = wave_row0 + 31 < rows;
   const int wave_jq0 = wave_row0 / heads;
 
@@ -535,6 +541,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // lanes of a row; l_part: this lane's share of the running sum.
     float m_ref[2] = {-INFINITY, -INFINITY};
     float l_part[2] = {0.f, 0.f};
+    float l_wt[2] = {0.f, 0.f};  // this lane's share of the sum of the bf16 weights
+    const bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
     float alpha[2] = {1.f, 1.f};
     bool any_scale = false;
     float mx[2], mu[2] = {kMuFloor, kMuFloor};
@@ -583,10 +591,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           const int hb = step - 9;
           const float m = mx[hb] * scale_log2;
           const bool upd = m > m_ref[hb] + kRescaleThreshold;
-          const float m_new = upd ? m : m_ref[hb];
+          const float m_new = upd ? (POW2 ? __builtin_ceilf(m) : m) : m_ref[hb];
           const float mu_new = fmaxf(m_new, kMuFloor);
-          alpha[hb] = __builtin_amdgcn_exp2f(mu[hb] - mu_new);
-          l_part[hb] *= alpha[hb];
+          if constexpr (POW2) {
+            // alpha holds the integer exponent mu - mu_new <= 0 (clamped:
+            // a first finite maximum scales a sum that is still 0).
+            alpha[hb] = fmaxf(mu[hb] - mu_new, -256.f);
+            l_part[hb] = __builtin_ldexpf(l_part[hb], (int)alpha[hb]);
+            l_wt[hb] = __builtin_ldexpf(l_wt[hb], (int)alpha[hb]);
+          } else {
+            alpha[hb] = __builtin_amdgcn_exp2f(mu[hb] - mu_new);
+            l_part[hb] *= alpha[hb];
+            l_wt[hb] *= alpha[hb];
+          }
           any_scale = any_scale || (upd && mu[hb] > kMuFloor);
           m_ref[hb] = m_new;
           mu[hb] = mu_new;
@@ -600,6 +617,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           if (kk & 1) {
             pw[hb][kk >> 1] = bf16x2{(__bf16)p_even, (__bf16)p};
             asm volatile("" : "+v"(pw[hb][kk >> 1]));  // pack now, not at the end
+            // The bf16 weights PV multiplies by, summed (one dot2 per pair):
+            // O is divided by this sum, so that a row stays a weighted mean
+            // of V rows under one set of weights (a row dominated by one key
+            // returns that key's V row, whatever the rounding of its weight);
+            // lse uses the exact sum.
+            l_wt[hb] = __builtin_amdgcn_fdot2_f32_bf16(pw[hb][kk >> 1], kOnes2, l_wt[hb], false);
           } else {
             p_even = p;
           }
@@ -711,7 +734,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
         // (tiles <= it).
         if (__any(any_scale)) {
           o_drain();
-          o_scale_all(alpha[0], alpha[1]);
+          if constexpr (POW2)
+            o_ldexp_rec<0>((int)alpha[0], (int)alpha[1]);
+          else
+            o_scale_all(alpha[0], alpha[1]);
+          ++n_rescale;
         }
         any_scale = false;
       } else {
@@ -734,6 +761,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     for (int hb = 0; hb < 2; ++hb) {
       l_tot[hb] = group_sum(l_part[hb]);
       lse_v[hb] = l_tot[hb] > 0.f ? (m_ref[hb] + __builtin_amdgcn_logf(l_tot[hb])) * kLn2 : -INFINITY;
+      l_tot[hb] = group_sum(l_wt[hb]);  // O's divisor from here on
       if (bad_len || bad_pg) lse_v[hb] = NAN;
     }
     if (sg.partial < 0) {
@@ -785,446 +813,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Ping-pong decode kernel (the default).  A workgroup of 8 waves holds the
-// 128 query rows of one row block; wave w owns rows 16w .. 16w+15 with their
-// whole query (rope part in LDS), their whole output O (512 columns, 128
-// AGPRs) and their own softmax state, so the waves share nothing but the tile
-// ring.  Waves w and w+4 run on the same SIMD (round-robin placement), and
-// they run half a tile apart:
-//   group 0 (w < 4):  phase A: QK^T(t)              phase B: softmax(t), PV(t)
-//   group 1 (w >= 4): phase A: softmax(t-1), PV(t-1) phase B: QK^T(t)
-// with one workgroup barrier at the end of each phase.  While one wave of a
-// SIMD runs its softmax on the vector unit, the other keeps the matrix pipe
-// busy: measured on gfx950, VALU work of another wave overlaps a wave's
-// MFMAs, while VALU work of the same wave is added to them.  Per tile and
-// SIMD that leaves the 2 x 68 MFMAs (2 x 1088 cycles) as the critical path.
-// Tiles are copied to the same 4-stage LDS ring as in decode_kernel (tile t
-// is read by group 0 in phases A(t), B(t) and by group 1 in phases B(t),
-// A(t+1); the copies of tile t+3 go into tile t-1's stage in phase B(t)).
-// The split partials use decode_kernel's fp16 format, so both combine
-// kernels serve both decode kernels.
-constexpr int kPpWaves = 8;
-constexpr int kPpRows = 16;                              // query rows per wave
-constexpr int kPpQpeWaveBytes = kPpRows * 64 * 2;        // rope part of a wave's rows in LDS
-static_assert(kPpWaves * kPpRows == kRowsPerBlock, "same row blocks as decode_kernel");
-static_assert(kStages * kStageBytes + kPpWaves * kPpQpeWaveBytes <= 160 * 1024, "LDS of one CU");
-
-// The output accumulators of a ping-pong wave: block cb (columns 16cb ..
-// 16cb+15 of the wave's 16 rows) is a[4cb : 4cb+3]; lane l holds row l%16,
-// columns 16cb + 4(l/16) + 0..3.
-template <int R>
-__device__ __forceinline__ void pp_zero_rec() {
-  if constexpr (R < 128) {
-    o_set<R>(0.f);
-    pp_zero_rec<R + 1>();
-  }
-}
-
-template <int R>
-__device__ __forceinline__ void pp_scale_rec(float alpha) {
-  if constexpr (R < 128) {
-    o_set<R>(o_get<R>() * alpha);
-    pp_scale_rec<R + 1>(alpha);
-  }
-}
-
-template <int CB>
-__device__ __forceinline__ void pp_store_rec(float* dst, float inv) {
-  if constexpr (CB < 32) {
-    constexpr int r = 4 * CB;
-    f32x4 w = {o_get<r + 0>() * inv, o_get<r + 1>() * inv, o_get<r + 2>() * inv, o_get<r + 3>() * inv};
-    store_wt(dst + 16 * CB, w);
-    pp_store_rec<CB + 1>(dst, inv);
-  }
-}
-
-template <int CB>
-__device__ __forceinline__ float pp_absmax_rec(float m) {
-  if constexpr (CB < 32) {
-    constexpr int r = 4 * CB;
-    float a, b;
-    asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(a) : "v"(m), "v"(o_get<r + 0>()), "v"(o_get<r + 1>()));
-    asm volatile("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(b) : "v"(a), "v"(o_get<r + 2>()), "v"(o_get<r + 3>()));
-    return pp_absmax_rec<CB + 1>(b);
-  }
-  return m;
-}
-
-// Partial store, decode_kernel's layout: column block pair (cb, cb+1) of a
-// row is 32 consecutive values, lane group g's 8 of them at [8g, 8g+8).
-template <int CB>
-__device__ __forceinline__ void pp_store_half_rec(_Float16* dst, float c) {
-  if constexpr (CB < 32) {
-    constexpr int r0 = 4 * CB, r1 = 4 * (CB + 1);
-    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-    f16x8 w = {(_Float16)(o_get<r0 + 0>() * c), (_Float16)(o_get<r0 + 1>() * c), (_Float16)(o_get<r0 + 2>() * c),
-               (_Float16)(o_get<r0 + 3>() * c), (_Float16)(o_get<r1 + 0>() * c), (_Float16)(o_get<r1 + 1>() * c),
-               (_Float16)(o_get<r1 + 2>() * c), (_Float16)(o_get<r1 + 3>() * c)};
-    store_wt(dst + 16 * CB, w);
-    pp_store_half_rec<CB + 2>(dst, c);
-  }
-}
-
-template <bool SINGLE_PAGE>
-__global__ __launch_bounds__(64 * kPpWaves, 1) void decode_pp_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
-    const uint8_t* __restrict__ cache, int64_t num_pages,
-    const int32_t* __restrict__ block_table, int32_t bt_stride,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ planned_lens,
-    const Segment* __restrict__ segs, const WorkgroupRange* __restrict__ wgs,
-    float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
-    float* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
-    float* __restrict__ ws_lse, float* __restrict__ ws_f) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kPpWaves * kPpQpeWaveBytes];
-  uint8_t* const qpe_lds = smem + kStages * kStageBytes;
-
-  const WorkgroupRange wr = wgs[blockIdx.x];
-  if (wr.seg_begin >= wr.seg_end) return;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = lane >> 4;
-  const int l16 = lane & 15;
-  const int rb = wr.row_block;
-  const int psize = 1 << page_log2;
-
-  // This lane's query row (16 rows per wave; row l16 of the wave).  Derived
-  // where it is needed from a lane index the compiler cannot see through, so
-  // that nothing per lane is kept alive across the tile loop for later use.
-  auto opaque_l16 = [&]() {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    return t & 15;
-  };
-  auto opaque_grp = [&]() {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    return (t >> 4) & 3;
-  };
-  const int wave_row0 = rb * kRowsPerBlock + wave * kPpRows;
-  const bool wave_full = wave_row0 + kPpRows - 1 < rows;
-  const int wave_jq0 = wave_row0 / heads;
-
-  // LDS operand addresses (per lane), as in decode_kernel: QK^T's key rows
-  // (key block 1 = bit 8 flipped) and PV's transposed V reads.
-  const int qk_off0 = 512 * grp + 16 * l16 + 256 * (grp & 1);
-  const int hsel = (l16 >> 1) & 1;
-  const int pv_off0 = 768 * hsel + 16 * (4 * grp + (l16 >> 2)) + 8 * (l16 & 1);
-  // Copies: wave w issues copies n = w + 8i of a tile (five for w < 4, four
-  // for w >= 4: 36 in all); lane l reads key row dma_row, bytes dma_col +
-  // 256 i of it, into LDS slot 64n + l.
-  const int dma_row = (lane & 31) ^ (16 * (lane >> 5));
-  const int dma_col = 16 * (lane >> 5) + 32 * wave;
-  // Rope part of the wave's query rows in LDS: row r (0..15) at
-  // wave * 2048 + 128 r, its 16-byte chunk c at slot c ^ ((r >> 1) & 7); the
-  // B operand of rope step e reads chunk 4e + grp of row l16.
-  const uint32_t qpe_base =
-      lds_addr(qpe_lds) + wave * kPpQpeWaveBytes + l16 * 128 + 16 * (grp ^ ((l16 >> 1) & 7));
-
-  for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
-    const Segment sg = segs[si];
-    const int b = sg.b, kv0 = sg.kv_begin, kv1 = sg.kv_end;
-    const int32_t* bt_row = block_table + (int64_t)b * bt_stride;
-    const int first_pg = kv0 >> page_log2;
-    const int last_pg = (kv1 - 1) >> page_log2;
-
-    // Every wave is done with the previous piece's stages and rope rows.
-    __syncthreads();
-
-    // The piece's first 64 page ids (one per lane), then the query rows: the
-    // no-rope part into registers (q[ks] = dims 32ks + 8grp .. +7 of row
-    // l16), the rope part into this wave's LDS slice (2 copies of 1 KB).
-    int pg_lane = load4(bt_row + min(first_pg + lane, last_pg));
-    bf16x8 q[kNopeSteps];
-    {
-      const int row = wave_row0 + opaque_l16();
-      const int qrow = row < rows ? row : 0;
-      const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * opaque_grp();
-#pragma unroll
-      for (int ks = 0; ks < kNopeSteps; ++ks) q[ks] = load16(qn + 32 * ks);
-    }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int pidx = n * 64 + lane;
-      const int r = pidx >> 3;
-      const int c = (pidx & 7) ^ ((r >> 1) & 7);
-      const int qr = wave_row0 + r;
-      const int qrow = qr < rows ? qr : 0;
-      dma16(q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * c, lds_addr(qpe_lds + wave * kPpQpeWaveBytes + n * 1024));
-    }
-
-    const int L = seq_lens[b];
-    const bool bad_len = (L != planned_lens[b]);
-    const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
-    // keys this lane's row may see inside the piece: [kv0, lim)
-    auto row_lim = [&]() {
-      const int row = wave_row0 + opaque_l16();
-      return row < rows ? min(kv1, L - q_len + 1 + row / heads) : kv0;
-    };
-
-    auto page_at = [&](int pidx) {
-      const int rel = pidx - first_pg;
-      if (rel < 64) return __builtin_amdgcn_readlane(pg_lane, rel);
-      // Further pages: a uniform index read through the constant address
-      // space (a scalar load, waited for with lgkmcnt, not vmcnt).
-      const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt_row;
-      return bt_s[__builtin_amdgcn_readfirstlane(pidx)];
-    };
-    auto fetch_pages = [&](int tb) {
-      TilePages tp;
-      tp.first = tb >> page_log2;
-      const int last = (min(tb + kTile, kv1) - 1) >> page_log2;
-      tp.pg[0] = page_at(tp.first);
-      tp.pg[1] = SINGLE_PAGE ? tp.pg[0] : page_at(min(tp.first + 1, last));
-      return tp;
-    };
-    // A page id outside [0, num_pages) is never followed: page 0 is read
-    // instead, and the piece's rows end as NaN (bad_pg), like a length mismatch.
-    const uint32_t num_pages_u32 = (uint32_t)min(num_pages, (int64_t)0x80000000LL);
-    bool bad_pg = false;
-    auto checked = [&](TilePages tp) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const bool ok = (uint32_t)tp.pg[k] < num_pages_u32;
-        bad_pg = bad_pg || !ok;
-        tp.pg[k] = ok ? tp.pg[k] : 0;
-      }
-      return tp;
-    };
-    struct TileSrc {
-      const uint8_t* base;
-      uint32_t off;
-      const uint8_t* ptr;
-    };
-    auto tile_src = [&](int tb, const TilePages& tp) {
-      TileSrc ts;
-      const int tok = min(tb + dma_row, kv1 - 1);
-      if (SINGLE_PAGE) {
-        ts.base = cache + ((int64_t)tp.pg[0] << page_log2) * kRowBytes;
-        ts.off = (uint32_t)((tok & (psize - 1)) * kRowBytes + dma_col);
-        ts.ptr = nullptr;
-      } else {
-        const int page = ((tok >> page_log2) == tp.first) ? tp.pg[0] : tp.pg[1];
-        ts.base = nullptr;
-        ts.off = 0;
-        ts.ptr = cache + (((int64_t)page << page_log2) + (tok & (psize - 1))) * kRowBytes + dma_col;
-      }
-      return ts;
-    };
-    // Copy i of this wave for a tile into `stage` (copy n = wave + 8i lands
-    // at stage + 1024 n; the immediate offset also moves the LDS destination).
-    auto dma = [&](auto ic, const TileSrc& ts, uint8_t* stage) {
-      constexpr int i = decltype(ic)::value;
-      const uint32_t dst = lds_addr(stage) + (uint32_t)((8 * i + wave) * 1024 - 256 * i);
-      if (SINGLE_PAGE)
-        dma16_saddr<256 * i>(ts.base, ts.off, dst);
-      else
-        dma16_off<256 * i>(ts.ptr, dst);
-    };
-
-    const int ntiles = (kv1 - kv0 + kTile - 1) / kTile;
-    const int last_tile = ntiles - 1;
-
-    // ---- softmax state (base 2, lazy reference), one value per lane ----
-    float m_ref = -INFINITY, mu = kMuFloor, l_part = 0.f;
-    o_drain();
-    pp_zero_rec<0>();
-
-    // Group g of this wave: 0 runs half-step k of the tile sequence in phase
-    // k, 1 runs it in phase k + 1 (half-step 2t = QK^T of tile t, 2t + 1 =
-    // softmax and PV of tile t).  One barrier ends every phase.
-    const int G = wave >> 2;
-    // Copies per tile: five for group 0 and four for group 1 (36 in all);
-    // the explicit waits count them.
-    auto dma_tile = [&](const TileSrc& ts, uint8_t* stage) {
-      static_for<4>([&](auto ic) { dma(ic, ts, stage); });
-      if (G == 0) dma(std::integral_constant<int, 4>{}, ts, stage);
-    };
-    auto wait_tiles = [&](auto nt_c) {  // own copies of all but the last nt tiles have landed
-      constexpr int nt = decltype(nt_c)::value;
-      if (G == 0)
-        wait_vmem<5 * nt>();
-      else
-        wait_vmem<4 * nt>();
-    };
-
-    // Page ids landed once only the query loads and rope copies are in flight.
-    wait_vmem<kNopeSteps + 2>();
-    asm volatile("" : "+v"(pg_lane));
-#pragma unroll
-    for (int st = 0; st < 3; ++st) {
-      const int tb_c = kv0 + min(st, last_tile) * kTile;
-      dma_tile(tile_src(tb_c, checked(fetch_pages(tb_c))), smem + st * kStageBytes);
-    }
-    TilePages pg_raw = fetch_pages(kv0 + min(3, last_tile) * kTile);
-    // Query rows, rope rows and tile 0 have landed once tiles 1 and 2 are the
-    // only copies in flight; the barrier publishes every wave's part.
-    wait_tiles(std::integral_constant<int, 2>{});
-    asm volatile("" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]), "+v"(q[6]),
-                 "+v"(q[7]));
-    asm volatile("" : "+v"(q[8]), "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]),
-                 "+v"(q[14]), "+v"(q[15]));
-    __syncthreads();
-
-    f32x4 s[2];  // scores of the tile between its QK^T and its softmax
-    for (int k = 0; k <= 2 * ntiles; ++k) {
-      const int j = k - G;  // this wave's half-step
-      const int t = j >> 1;
-      const uint8_t* cur = smem + ((t & (kStages - 1)) * kStageBytes);
-      // Odd phases carry the copies of tile (k >> 1) + 3 into the stage of
-      // tile (k >> 1) - 1, free since the previous barrier.
-      const bool copies = (k & 1) != 0;
-      const int nt = (k >> 1) + 3;
-      const int tb_c = kv0 + min(nt, last_tile) * kTile;
-      uint8_t* nbuf = smem + (nt % kStages) * kStageBytes;
-      const TileSrc nsrc = tile_src(tb_c, checked(pg_raw));
-      // copy i of this wave between MFMAs i * every (uniform branches)
-      auto copy_at = [&](int m, int every) {
-        if (copies && m % every == 0)
-          static_for<5>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if (i == m / every && (i < 4 || G == 0)) dma(ic, nsrc, nbuf);
-          });
-      };
-
-      if (j >= 0 && j < 2 * ntiles) {
-        if ((j & 1) == 0) {
-          // ---- QK^T of tile t ----
-          const uint32_t k0 = lds_addr(cur) + qk_off0, k1 = k0 ^ 256u;
-          bf16x8 a[2][2];
-          bf16x8 qb;
-          auto read = [&](int ks) {
-            a[ks & 1][0] = *LDS_AS(const bf16x8, (uintptr_t)(k0 + 2048 * ks));
-            a[ks & 1][1] = *LDS_AS(const bf16x8, (uintptr_t)(k1 + 2048 * ks));
-          };
-          read(0);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < kQSteps; ++ks) {
-            if (ks + 1 < kQSteps) read(ks + 1);
-            if (ks >= kNopeSteps) qb = *LDS_AS(const bf16x8, (uintptr_t)(ks == kNopeSteps ? qpe_base : qpe_base ^ 64u));
-            const bf16x8& bq = ks < kNopeSteps ? q[ks] : qb;
-            s_mfma(s[0], a[ks & 1][0], bq, ks == 0);
-            copy_at(2 * ks, 8);
-            __builtin_amdgcn_sched_barrier(0);
-            s_mfma(s[1], a[ks & 1][1], bq, ks == 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          s_mfma_drain2(s);
-        } else {
-          // ---- softmax of tile t: mask, row maximum, lazy reference update,
-          //      weights 2^(s * scale - mu) into the P^T operand (K slot j < 4 of
-          //      lane group g is key 4g + j, slot j >= 4 key 16 + 4g + j - 4:
-          //      the lane's own scores), running sum ----
-          const int tb_s = kv0 + t * kTile;
-          if (__builtin_amdgcn_readfirstlane((int)(tb_s + kTile > lim_wave))) {
-            const int lim = row_lim();
-            const int k4 = tb_s + 4 * opaque_grp();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) s[kb][i] = (k4 + 16 * kb + i < lim) ? s[kb][i] : -INFINITY;
-          }
-          float mx = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[1][0], s[1][1]),
-                          max3(s[1][2], s[1][3], s[1][3]));
-          mx = group_max16(group_max32(mx));
-          const float m = mx * scale_log2;
-          const bool upd = m > m_ref + kRescaleThreshold;
-          const float m_new = upd ? m : m_ref;
-          const float mu_new = fmaxf(m_new, kMuFloor);
-          const float alpha = __builtin_amdgcn_exp2f(mu - mu_new);
-          const bool rescale = upd && mu > kMuFloor;
-          l_part *= alpha;
-          m_ref = m_new;
-          mu = mu_new;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, -mu));
-          l_part += ((s[0][0] + s[0][1]) + (s[0][2] + s[0][3])) + ((s[1][0] + s[1][1]) + (s[1][2] + s[1][3]));
-          const bf16x8 pb = bf16x8{(__bf16)s[0][0], (__bf16)s[0][1], (__bf16)s[0][2], (__bf16)s[0][3],
-                                   (__bf16)s[1][0], (__bf16)s[1][1], (__bf16)s[1][2], (__bf16)s[1][3]};
-          // A row whose reference moved rescales everything accumulated so far.
-          if (__any(rescale)) {
-            o_drain();
-            pp_scale_rec<0>(alpha);
-            asm volatile("s_nop 4" ::: "memory");
-          }
-          // ---- PV of tile t: 32 column blocks, V^T read transposed from the
-          //      stage (two 8-byte reads per block), two blocks ahead ----
-          const uint32_t r0 = lds_addr(cur) + pv_off0, r1 = r0 ^ 256u;
-          i16x4 v[3][2];
-          auto rv = [&](int cb, int rd) {
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(i16x4, (uintptr_t)((rd ? r1 : r0) + 1024 * cb)));
-          };
-          v[0][0] = rv(0, 0);
-          v[0][1] = rv(0, 1);
-          v[1][0] = rv(1, 0);
-          v[1][1] = rv(1, 1);
-          __builtin_amdgcn_sched_barrier(0);
-          static_for<32>([&](auto cbc) {
-            constexpr int cb = decltype(cbc)::value;
-            if constexpr (cb + 2 < 32) {
-              v[(cb + 2) % 3][0] = rv(cb + 2, 0);
-              v[(cb + 2) % 3][1] = rv(cb + 2, 1);
-            }
-            const bf16x8 va =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[cb % 3][0], v[cb % 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
-            OBlock<cb>::mfma(va, pb);
-            copy_at(cb, 6);
-            __builtin_amdgcn_sched_barrier(0);
-          });
-        }
-      }
-      if (copies) {
-        // the odd phase issued tile (k >> 1) + 3: tile (k >> 1) + 1 has
-        // landed once only tiles (k >> 1) + 2 and + 3 are in flight
-        wait_tiles(std::integral_constant<int, 2>{});
-        pg_raw = fetch_pages(kv0 + min(nt + 1, last_tile) * kTile);
-      }
-      __syncthreads();
-    }
-
-    // The repeated copies past the end of the piece must land before the next
-    // piece reuses their stages.
-    wait_vmem<0>();
-
-    // ---- epilogue ----
-    o_drain();
-    const float l_tot = group_sum(l_part);
-    float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    if (bad_len || bad_pg) lse_v = NAN;
-    const int row_e = wave_row0 + opaque_l16();
-    const int grp_e = opaque_grp();
-    if (sg.partial < 0) {
-      float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      if (bad_len || bad_pg) inv = NAN;
-      if (row_e < rows) {
-        const int64_t oi = (int64_t)b * rows + row_e;
-        pp_store_rec<0>(out + oi * 512 + 4 * grp_e, inv);
-        if (grp_e == 0) lse[oi] = lse_v;
-      }
-    } else {
-      const int64_t slot = (int64_t)sg.partial * nrb + rb;
-      float amax = pp_absmax_rec<0>(0.f);
-      amax = group_max16(group_max32(amax));
-      const int e = max(__builtin_amdgcn_frexp_expf(amax), -110);
-      const float c = __builtin_ldexpf(1.f, 15 - e);
-      float f = l_tot > 0.f ? __builtin_ldexpf(1.f / l_tot, e - 15) : 0.f;
-      if (bad_len || bad_pg) f = NAN;
-      if (row_e < rows) {
-        const int64_t ri = slot * kRowsPerBlock + (row_e - rb * kRowsPerBlock);
-        pp_store_half_rec<0>(reinterpret_cast<_Float16*>(ws_o) + ri * 512 + 8 * grp_e, c);
-        if (grp_e == 0) {
-          ws_lse[ri] = lse_v;
-          ws_f[ri] = f;
-        }
-      }
-    }
-  }
+  // After the last piece: no tile copy is in flight any more.
+  if (rescale_events != nullptr && n_rescale != 0 && lane == 0) atomicAdd(rescale_events, n_rescale);
 }
 
 // One workgroup = one row of one split request (the unit's row0).  Stored position 8l + e of a
@@ -1560,25 +1150,22 @@ mla_status scratch_address(int device, void** addr) {
   return MLA_OK;
 }
 
-template <bool SINGLE_PAGE>
+template <bool SINGLE_PAGE, bool POW2>
 hipError_t launch_decode(const mla_plan* plan, const void* q_nope, const void* q_pe, const void* cache,
                          int64_t num_pages, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
-                         float scale_log2, float* out, float* lse, const Workspace& ws, hipStream_t stream) {
+                         float scale_log2, float* out, float* lse, const Workspace& ws, uint32_t* rescale_events,
+                         hipStream_t stream) {
   const mla::PlanData& d = plan->d;
   const char* base = static_cast<const char*>(plan->dev);
   int page_log2 = 0;
   while ((1 << page_log2) < d.page) ++page_log2;
-#if MLA_PP
-  hipLaunchKernelGGL((mla::decode_pp_kernel<SINGLE_PAGE>), dim3(d.grid), dim3(64 * mla::kPpWaves), 0, stream,
-#else
-  hipLaunchKernelGGL((mla::decode_kernel<SINGLE_PAGE>), dim3(d.grid), dim3(64 * mla::kWaves), 0, stream,
-#endif
+  hipLaunchKernelGGL((mla::decode_kernel<SINGLE_PAGE, POW2>), dim3(d.grid), dim3(64 * mla::kWaves), 0, stream,
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
                      static_cast<const uint8_t*>(cache), num_pages, bt, bt_stride, seq_lens,
                      reinterpret_cast<const int32_t*>(base + plan->off_lens),
                      reinterpret_cast<const mla::Segment*>(base + plan->off_segs),
                      reinterpret_cast<const mla::WorkgroupRange*>(base + plan->off_wgs), scale_log2, d.rows,
-                     d.heads, d.q_len, page_log2, d.nrb, out, lse, ws.o, ws.lse, ws.f);
+                     d.heads, d.q_len, page_log2, d.nrb, out, lse, ws.o, ws.lse, ws.f, rescale_events);
   return hipGetLastError();
 }
 
@@ -1673,11 +1260,15 @@ mla_status mla_plan_copy_combine(const mla_plan* plan, int32_t* unit) {
   return MLA_OK;
 }
 
-mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
-                               const void* kv_cache, int64_t num_pages, const int32_t* block_table, int32_t bt_stride,
-                               const int32_t* seq_lens, float softmax_scale, float* out, float* lse, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static mla_status decode_partials(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
+                                  const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                  int32_t bt_stride, const int32_t* seq_lens, float softmax_scale, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes, int32_t variant,
+                                  uint32_t* rescale_events, void* stream) {
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (variant != MLA_RESCALE_LAZY && variant != MLA_RESCALE_POW2)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "variant must be MLA_RESCALE_LAZY or MLA_RESCALE_POW2");
+  if (!aligned(rescale_events, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "rescale_events must be 4-byte aligned");
   if (!q_nope_absorbed || !q_pe || !kv_cache || !block_table || !seq_lens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
   if (!aligned(q_nope_absorbed, 16) || !aligned(q_pe, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
@@ -1703,13 +1294,36 @@ mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed
   const bool single = d.page >= d.v.tile_tokens;
   if (d.v.waves != mla::kWaves || d.v.tile_tokens != mla::kTile)
     return fail(MLA_ERR_INVALID_ARGUMENT, "plan was not made by mla_decode_plan (an FP8 plan runs with mla_decode_fp8)");
-  hipError_t e = single ? launch_decode<true>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride,
-                                                 seq_lens, scale_log2, out, lse, ws, st)
-                        : launch_decode<false>(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table,
-                                                  bt_stride, seq_lens, scale_log2, out, lse, ws, st);
+  auto launch = [&](auto single_c, auto pow2_c) {
+    return launch_decode<decltype(single_c)::value, decltype(pow2_c)::value>(
+        plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens, scale_log2, out, lse, ws,
+        rescale_events, st);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  const bool pow2 = variant == MLA_RESCALE_POW2;
+  hipError_t e = single ? (pow2 ? launch(T{}, T{}) : launch(T{}, F{})) : (pow2 ? launch(F{}, T{}) : launch(F{}, F{}));
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   g_last_error.clear();
   return MLA_OK;
+}
+
+mla_status mla_decode_partials(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
+                               const void* kv_cache, int64_t num_pages, const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, float softmax_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return decode_partials(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens,
+                         softmax_scale, out, lse, workspace, workspace_bytes, MLA_RESCALE_LAZY, nullptr, stream);
+}
+
+mla_status mla_decode_variant(const mla_plan* plan, const void* q_nope_absorbed, const void* q_pe,
+                              const void* kv_cache, int64_t num_pages, const int32_t* block_table, int32_t bt_stride,
+                              const int32_t* seq_lens, float softmax_scale, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, int32_t variant, uint32_t* rescale_events, void* stream) {
+  mla_status s = decode_partials(plan, q_nope_absorbed, q_pe, kv_cache, num_pages, block_table, bt_stride, seq_lens,
+                                 softmax_scale, out, lse, workspace, workspace_bytes, variant, rescale_events, stream);
+  if (s != MLA_OK) return s;
+  return mla_decode_combine(plan, out, lse, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse, void* workspace, size_t workspace_bytes,

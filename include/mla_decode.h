@@ -192,6 +192,42 @@ mla_status mla_decode_combine(const mla_plan* plan, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_variant -- mla_decode with a choice of how the online softmax
+ * rescales O, and an optional count of the rescales.
+ *
+ * The Huawei report ("DeepSeek V3/R1 inference deployment best practices on
+ * Ascend servers", section 6.1 on the MLA operator, the AMLA bullet) turns the
+ * multiplicative update of O into an additive one by working on the float's
+ * binary encoding.  Here both forms keep a lazy reference (a row moves it only
+ * when its maximum grows by more than 2^8):
+ *  variant MLA_RESCALE_LAZY (0): the reference is the row maximum itself and
+ *    O, l are multiplied by 2^(mu_old - mu_new) (what mla_decode runs);
+ *  variant MLA_RESCALE_POW2 (1): the reference is the row maximum rounded up
+ *    to an integer (log2 units), so the factor is an exact power of two and O,
+ *    l are updated by adding to their exponents (v_ldexp_f32, which also keeps
+ *    zeros and underflow right); l sums the bf16-rounded weights that multiply
+ *    V (with an integer reference even a row's largest weight is rounded, and
+ *    one set of weights keeps O / l a weighted mean).
+ * Both give the same result up to rounding (each within the bar of mla_decode).
+ *  rescale_events   NULL, or a device uint32 that the call adds to: one per
+ *                   wave (32 query rows) and tile after which that wave
+ *                   rescaled its O; 4-byte aligned; the caller zeroes it.
+ * Other arguments, checks and errors as for mla_decode; an unknown variant is
+ * MLA_ERR_INVALID_ARGUMENT.
+ */
+#define MLA_RESCALE_LAZY 0
+#define MLA_RESCALE_POW2 1
+mla_status mla_decode_variant(const mla_plan* plan,
+                              const void* q_nope_absorbed, const void* q_pe,
+                              const void* kv_cache, int64_t num_pages,
+                              const int32_t* block_table, int32_t bt_stride,
+                              const int32_t* seq_lens, float softmax_scale,
+                              float* out, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t variant, uint32_t* rescale_events,
+                              void* stream);
+
+/*
  * FP8 latent cache.
  *
  * The Huawei report ("DeepSeek V3/R1 inference deployment best practices on

@@ -31,7 +31,9 @@ def asm(tmp_path_factory):
 
 def test_decode_kernels_present(asm):
     bodies = asm_checks.kernel_bodies(asm)
-    assert len(bodies) == 2  # one page per tile / two pages per tile
+    # one page per tile / two pages per tile, each with the lazy and the
+    # power-of-two rescale
+    assert len(bodies) == 4
     for b in bodies:
         assert sum(t.startswith("v_mfma_f32_16x16x32_bf16") for t in b) >= 136
 
@@ -68,7 +70,7 @@ def test_accumulators_only_touched_by_inline_asm(asm):
 
 def test_decode_kernels_do_not_spill(asm):
     res = {k: v for k, v in asm_checks.kernel_resources(asm).items() if k.startswith(asm_checks.DECODE_PREFIX)}
-    assert len(res) == 2
+    assert len(res) == 4
     for name, r in res.items():
         # no VGPR spills and no scratch memory at all (spilled SGPRs go to
         # lanes of a VGPR, not to memory)
