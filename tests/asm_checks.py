@@ -14,7 +14,15 @@ kernel's comments promise:
     (the compiler adds none: an extra one would serialize the copy pipeline);
   * no VALU instruction overwrites the data registers of a preceding store of
     more than 8 bytes in the next wait state (gfx9-family store data hazard;
-    the asm stores carry their own s_nop).
+    the asm stores carry their own s_nop);
+  * no VALU write of an SGPR is followed within 5 wait states by a vector
+    memory instruction reading that SGPR (the asm copies take SGPR bases);
+  * nothing but the next MFMA of the same accumulation chain reads or writes
+    an MFMA's destination registers within 19 wait states (the matrix unit
+    writes its result long after issue; a register the compiler reused right
+    after an asm MFMA would race with that write).
+The last two are for kernels whose MFMAs are inline asm: for MFMAs the
+compiler emits itself it inserts the exact, shape-specific wait states.
 """
 from __future__ import annotations
 
@@ -257,3 +265,99 @@ def kernel_resources(asm: str) -> dict:
             if m:
                 res[cur][key] = int(m.group(1))
     return res
+
+
+def _sgprs(tok: str) -> set:
+    tok = tok.strip().rstrip(",")
+    m = re.match(r"s\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    if m:
+        return {int(m.group(1))}
+    if tok == "vcc":
+        return {106, 107}
+    if tok in ("vcc_lo", "vcc_hi"):
+        return {106 if tok == "vcc_lo" else 107}
+    return set()
+
+
+def _wait_states(op: str, ops: list) -> int:
+    if op == "s_nop":
+        return int(ops[0], 0) + 1 if ops else 1
+    return 1
+
+
+def sgpr_vmem_hazards(body: list, need: int = 5) -> list:
+    """A VALU write of an SGPR (v_readfirstlane, v_readlane, v_cmp to an SGPR
+    pair, a carry out) followed by a vector-memory instruction that reads that
+    SGPR as an address or offset needs `need` wait states in between (gfx9
+    family).  The compiler inserts them between its own instructions but does
+    not look inside inline asm, and the LDS copies and stores are inline asm
+    taking SGPR bases.  Returns (index, vmem line, writer line) per violation."""
+    bad = []
+    last_write = {}  # sgpr -> (wait-state position after the writer, line)
+    pos = 0
+    for i, line in enumerate(body):
+        op, ops = _split(line)
+        if op.startswith(("global_", "buffer_", "flat_", "scratch_")):
+            for o in (w for o in ops for w in o.split()):
+                for s in _sgprs(o):
+                    if s in last_write and pos - last_write[s][0] < need:
+                        bad.append((i, line, last_write[s][1]))
+        if op.startswith("v_") and not op.startswith(("v_mfma", "v_accvgpr")) and ops:
+            dests = [ops[0]]
+            if "_co_" in op or "div_scale" in op:
+                dests.append(ops[1] if len(ops) > 1 else "")
+            for d in dests:
+                for s in _sgprs(d):
+                    last_write[s] = (pos + 1, line)
+        elif op.startswith("s_") and ops and not op.startswith(("s_waitcnt", "s_nop", "s_cbranch", "s_branch", "s_barrier")):
+            # an SALU write clears the VALU-write record of that SGPR
+            for s in _sgprs(ops[0]):
+                last_write.pop(s, None)
+        pos += _wait_states(op, ops)
+    return bad
+
+
+def _all_regs(tok: str) -> set:
+    out = set()
+    for w in tok.split():
+        out |= _regs(w)
+    return out
+
+
+def mfma_dst_races(body: list, need: int = 19) -> list:
+    """Instructions that read or write an MFMA's destination registers (VGPR or
+    AGPR) within `need` wait states of the MFMA, other than a following MFMA
+    that takes exactly that destination as its accumulator (srcC) and writes
+    it again (an accumulation chain, which the hardware interlocks).  The
+    matrix unit writes its result many cycles after issue; the compiler does
+    not know an inline-asm MFMA's latency, so a register it considers free
+    right after the asm, or a read that it schedules next to it, would race
+    with that late write.  Returns (mfma line, racing line) pairs."""
+    bad = []
+    for i, t in enumerate(body):
+        op, ops = _split(t)
+        if not op.startswith("v_mfma") or len(ops) < 4:
+            continue
+        dst = _all_regs(ops[0])
+        left, j = need, i + 1
+        while left > 0 and j < len(body):
+            uop, uops = _split(body[j])
+            if uop == "s_nop":
+                left -= int(uops[0], 0) + 1
+                j += 1
+                continue
+            regs = [_all_regs(o) for o in uops]
+            if uop.startswith("v_mfma") and len(uops) >= 4:
+                chain = regs[3] == dst and regs[0] == dst
+                if not chain and any(r & dst for r in regs):
+                    bad.append((t, body[j]))
+                    break
+            elif any(r & dst for r in regs):
+                bad.append((t, body[j]))
+                break
+            left -= 1
+            j += 1
+    return bad

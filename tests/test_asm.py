@@ -84,6 +84,20 @@ def test_every_load_result_waited_for(asm):
         assert asm_checks.pending_load_violations(body) == []
 
 
+def test_no_sgpr_write_to_vmem_hazards(asm):
+    # the copies and stores are inline asm with SGPR bases: no VALU write of
+    # such an SGPR within 5 wait states before them (whole kernel bodies)
+    for body in asm_checks.kernel_bodies(asm, whole=True):
+        assert asm_checks.sgpr_vmem_hazards(body) == []
+
+
+def test_no_mfma_destination_races(asm):
+    # nothing but the next MFMA of the same accumulation chain touches an
+    # inline-asm MFMA's result registers (VGPR or AGPR) within 19 wait states
+    for body in asm_checks.kernel_bodies(asm, whole=True):
+        assert asm_checks.mfma_dst_races(body) == []
+
+
 def test_page_ids_not_loaded_by_vector_loads(asm):
     # one vector dword load (the piece's first 64 page ids, waited for
     # explicitly); pages further on come from scalar loads, never from a vector
@@ -158,6 +172,16 @@ def test_fp8_only_explicit_vmcnt_waits(asm_fp8):
 def test_fp8_every_load_result_waited_for(asm_fp8):
     for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX):
         assert asm_checks.pending_load_violations(body) == []
+
+
+def test_fp8_no_sgpr_write_to_vmem_hazards(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX, whole=True):
+        assert asm_checks.sgpr_vmem_hazards(body) == []
+
+
+def test_fp8_no_mfma_destination_races(asm_fp8):
+    for body in asm_checks.kernel_bodies(asm_fp8, prefix=FP8_PREFIX, whole=True):
+        assert asm_checks.mfma_dst_races(body) == []
 
 
 def test_fp8_page_ids_not_loaded_by_vector_loads(asm_fp8):
