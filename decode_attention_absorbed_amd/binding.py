@@ -58,6 +58,7 @@ EXPORTED = (
     "mla_o_project",
     "mla_decode_noalloc",
     "mla_decode_variant",
+    "mla_decode_plan_update",
 )
 
 #: values of mla_decode_variant's `variant` (include/mla_decode.h)
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_plan.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
     L.mla_decode_plan.restype = ctypes.c_int
     L.mla_decode_plan_host.argtypes = L.mla_decode_plan.argtypes
+    L.mla_decode_plan_update.argtypes = [vp, i32p, vp]
+    L.mla_decode_plan_update.restype = ctypes.c_int
     L.mla_decode_plan_host.restype = ctypes.c_int
     L.mla_decode_workspace_bytes.argtypes = [vp]
     L.mla_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -196,6 +199,18 @@ class Plan:
         cu = np.zeros((max(n, 1), 4), dtype=np.int32)
         _check(lib().mla_plan_copy_combine(self.handle, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return cu[:n]
+
+    def update(self, seq_lens: Sequence[int], stream: Optional["torch.cuda.Stream"] = None) -> None:
+        """mla_decode_plan_update: new lengths for the same batch shape, copied
+        to the device schedule on `stream` (default: the current stream)."""
+        lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        if lens.shape != (self.batch,):
+            raise ValueError(f"seq_lens: shape {lens.shape}, expected ({self.batch},)")
+        if stream is None and self.on_device:
+            stream = torch.cuda.current_stream()
+        st = stream.cuda_stream if stream is not None else None
+        _check(lib().mla_decode_plan_update(self.handle, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), st))
+        self.seq_lens = lens
 
     def destroy(self) -> None:
         if self.handle:

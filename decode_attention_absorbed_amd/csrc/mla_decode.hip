@@ -1000,8 +1000,15 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 struct mla_plan {
   mla::PlanData d;
-  void* dev = nullptr;  // device schedule: segs | wgs | combine units | planned lens
-  size_t off_segs = 0, off_wgs = 0, off_units = 0, off_lens = 0;
+  int32_t variant = 1;  // planner variant (1: bf16 kernel, 2: FP8 kernel)
+  // Device schedule: segs | wgs | combine units | planned lens, each region
+  // sized for the largest schedule any lengths can give at this batch, query
+  // length, head count and CU count, so that an update never reallocates.
+  void* dev = nullptr;
+  size_t off_segs = 0, off_wgs = 0, off_units = 0, off_lens = 0, total = 0;
+  size_t cap_segs = 0, cap_wgs = 0, cap_units = 0;
+  void* stage = nullptr;        // pinned host copy of the schedule (source of the uploads)
+  hipEvent_t staged = nullptr;  // recorded after the last upload from `stage`
   int device = -1;
 };
 
@@ -1019,6 +1026,24 @@ mla_status hip_fail(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Writes schedule d into the plan's pinned staging copy (the region layout
+// is fixed at creation).
+void stage_schedule(mla_plan* p, const mla::PlanData& d) {
+  char* h = static_cast<char*>(p->stage);
+  std::memcpy(h + p->off_segs, d.segs.data(), d.segs.size() * sizeof(mla::Segment));
+  std::memcpy(h + p->off_wgs, d.wgs.data(), d.wgs.size() * sizeof(mla::WorkgroupRange));
+  if (!d.cunits.empty()) std::memcpy(h + p->off_units, d.cunits.data(), d.cunits.size() * sizeof(mla::CombineUnit));
+  std::memcpy(h + p->off_lens, d.lens.data(), d.lens.size() * sizeof(int32_t));
+}
+
+void release_plan(mla_plan* p) {
+  if (p->staged) (void)hipEventSynchronize(p->staged);
+  if (p->dev) (void)hipFree(p->dev);
+  if (p->stage) (void)hipHostFree(p->stage);
+  if (p->staged) (void)hipEventDestroy(p->staged);
+  delete p;
+}
 
 mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
                      int32_t page_size, int32_t num_cus, mla_plan** plan_out, bool upload, int32_t variant = 1) {
@@ -1051,6 +1076,7 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
     delete p;
     return fail((mla_status)rc, err);
   }
+  p->variant = variant;
   if (upload) {
     if (device < 0) {
       hipError_t e = hipGetDevice(&device);
@@ -1061,28 +1087,30 @@ mla_status make_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
     }
     p->device = device;
     const mla::PlanData& d = p->d;
+    // Largest schedule at this shape: at most max_slots slots of nrb
+    // workgroups, one piece per request plus one per slot boundary, the grid
+    // rounded up to whole XCD blocks of row blocks, one combine unit per split
+    // row (and padding to the XCD count).
+    const int64_t max_slots = std::max<int64_t>(1, (int64_t)d.num_cus * d.v.wg_per_cu / d.nrb);
+    p->cap_segs = std::max<size_t>(d.segs.size(), (size_t)(d.batch + max_slots));
+    p->cap_wgs = std::max<size_t>(d.wgs.size(), (size_t)(max_slots * d.nrb + mla::kNumXcd * (d.nrb + 1)));
+    p->cap_units = std::max<size_t>(d.cunits.size(), (size_t)d.batch * d.rows + mla::kNumXcd);
     p->off_segs = 0;
-    p->off_wgs = align256(d.segs.size() * sizeof(mla::Segment));
-    p->off_units = p->off_wgs + align256(d.wgs.size() * sizeof(mla::WorkgroupRange));
-    p->off_lens = p->off_units + align256(d.cunits.size() * sizeof(mla::CombineUnit));
-    const size_t total = p->off_lens + align256(d.lens.size() * sizeof(int32_t));
-    std::string host(total, '\0');
-    std::memcpy(&host[p->off_segs], d.segs.data(), d.segs.size() * sizeof(mla::Segment));
-    std::memcpy(&host[p->off_wgs], d.wgs.data(), d.wgs.size() * sizeof(mla::WorkgroupRange));
-    if (!d.cunits.empty())
-      std::memcpy(&host[p->off_units], d.cunits.data(), d.cunits.size() * sizeof(mla::CombineUnit));
-    std::memcpy(&host[p->off_lens], d.lens.data(), d.lens.size() * sizeof(int32_t));
-    hipError_t e = hipMalloc(&p->dev, total);
-    if (e != hipSuccess) {
-      delete p;
-      return e == hipErrorOutOfMemory ? fail(MLA_ERR_OUT_OF_MEMORY, "hipMalloc of the plan schedule failed")
-                                      : hip_fail(e, "hipMalloc");
+    p->off_wgs = align256(p->cap_segs * sizeof(mla::Segment));
+    p->off_units = p->off_wgs + align256(p->cap_wgs * sizeof(mla::WorkgroupRange));
+    p->off_lens = p->off_units + align256(p->cap_units * sizeof(mla::CombineUnit));
+    p->total = p->off_lens + align256((size_t)d.batch * sizeof(int32_t));
+    hipError_t e = hipMalloc(&p->dev, p->total);
+    if (e == hipSuccess) e = hipHostMalloc(&p->stage, p->total, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->staged, hipEventDisableTiming);
+    if (e == hipSuccess) {
+      stage_schedule(p, p->d);
+      e = hipMemcpy(p->dev, p->stage, p->total, hipMemcpyHostToDevice);
     }
-    e = hipMemcpy(p->dev, host.data(), total, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-      (void)hipFree(p->dev);
-      delete p;
-      return hip_fail(e, "hipMemcpy of the plan schedule");
+      release_plan(p);
+      return e == hipErrorOutOfMemory ? fail(MLA_ERR_OUT_OF_MEMORY, "allocation of the plan schedule failed")
+                                      : hip_fail(e, "upload of the plan schedule");
     }
   }
   *plan_out = p;
@@ -1193,9 +1221,40 @@ mla_status mla_decode_plan_host(const int32_t* seq_lens_host, int32_t batch, int
 size_t mla_decode_workspace_bytes(const mla_plan* plan) { return plan ? mla::workspace_bytes(plan->d) : 0; }
 
 void mla_decode_plan_destroy(mla_plan* plan) {
-  if (!plan) return;
-  if (plan->dev) (void)hipFree(plan->dev);
-  delete plan;
+  if (plan) release_plan(plan);
+}
+
+mla_status mla_decode_plan_update(mla_plan* plan, const int32_t* seq_lens_host, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!seq_lens_host) return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens_host is NULL");
+  if (!plan->dev) return fail(MLA_ERR_INVALID_ARGUMENT, "plan was made by a _plan_host call and has no device schedule");
+  mla_status st_dev = check_device(plan);
+  if (st_dev != MLA_OK) return st_dev;
+  const mla::PlanData& old = plan->d;
+  mla::PlanData next;
+  std::string err;
+  int rc;
+  try {
+    mla::PlanTuning tuning;
+    tuning.variant = plan->variant;
+    rc = mla::build_plan(seq_lens_host, old.batch, old.q_len, old.heads, old.page, old.num_cus, tuning, &next, &err);
+  } catch (const std::bad_alloc&) {
+    return fail(MLA_ERR_OUT_OF_MEMORY, "host allocation failed while planning");
+  }
+  if (rc != 0) return fail((mla_status)rc, err);
+  if (next.segs.size() > plan->cap_segs || next.wgs.size() > plan->cap_wgs || next.cunits.size() > plan->cap_units)
+    return fail(MLA_ERR_UNSUPPORTED, "the new schedule does not fit the room reserved at creation");
+  // The previous upload must have left the staging copy before it is rewritten.
+  hipError_t e = hipEventSynchronize(plan->staged);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize on the previous schedule upload");
+  stage_schedule(plan, next);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(plan->dev, plan->stage, plan->total, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipEventRecord(plan->staged, st);
+  if (e != hipSuccess) return hip_fail(e, "upload of the updated schedule");
+  plan->d = std::move(next);
+  g_last_error.clear();
+  return MLA_OK;
 }
 
 const char* mla_status_string(mla_status s) {

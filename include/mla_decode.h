@@ -54,9 +54,10 @@ typedef enum {
   MLA_ERR_OUT_OF_MEMORY = 5       /* host or device allocation failed while planning        */
 } mla_status;
 
-/* Opaque split plan.  Immutable after creation; may be shared by any number of
- * mla_decode calls (e.g. by every layer of one decode step), concurrently too,
- * as long as concurrent calls use separate workspaces. */
+/* Opaque split plan.  Changed only by mla_decode_plan_update; otherwise it may
+ * be shared by any number of mla_decode calls (e.g. by every layer of one
+ * decode step), concurrently too, as long as concurrent calls use separate
+ * workspaces. */
 typedef struct mla_plan mla_plan;
 
 /*
@@ -73,14 +74,38 @@ typedef struct mla_plan mla_plan;
  *  num_cus        compute units to plan for; 0 = ask the current device.
  *  plan_out       receives the new plan (set to NULL on failure).
  *
- * Allocates host memory and a small device buffer holding the schedule (it
- * calls hipMalloc/hipMemcpy on the current device).  Release with
- * mla_decode_plan_destroy.  Errors: MLA_ERR_INVALID_ARGUMENT,
- * MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_MEMORY, MLA_ERR_HIP.
+ * Allocates host memory, pinned host memory and a small device buffer holding
+ * the schedule (hipMalloc, hipHostMalloc and a synchronous hipMemcpy on the
+ * current device); per-step re-planning without any of these is
+ * mla_decode_plan_update.  Release with mla_decode_plan_destroy.  Errors:
+ * MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_OUT_OF_MEMORY,
+ * MLA_ERR_HIP.
  */
 mla_status mla_decode_plan(const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
                            int32_t num_heads, int32_t page_size, int32_t num_cus,
                            mla_plan** plan_out);
+
+/*
+ * mla_decode_plan_update -- re-plan in place for new sequence lengths, for a
+ * serving loop that re-plans every decode step: same batch, q_len, num_heads,
+ * page_size and CU count as at creation, new seq_lens_host (host int32
+ * [batch], checked as in mla_decode_plan).  Allocates nothing and never
+ * synchronizes the device: the new schedule is copied to the plan's device
+ * memory with hipMemcpyAsync on `stream` (hipStream_t; NULL = the default
+ * stream) from pinned host memory the plan owns (reserved at creation, sized
+ * for the largest schedule of its shape).  Stream order decides which
+ * schedule a call sees: decode calls enqueued on `stream` before the update
+ * run the old schedule, later ones the new.  Only the host waits, and only
+ * for the previous update's copy to have left the pinned memory.  Callers
+ * must not update a plan while another thread uses it, nor while calls on
+ * other streams may still read it.  mla_decode_workspace_bytes may change:
+ * query it again.  Errors: MLA_ERR_INVALID_ARGUMENT (NULL arguments, lengths
+ * out of range, a plan from a _plan_host call, another current device; the
+ * plan is unchanged), MLA_ERR_UNSUPPORTED (the schedule exceeds the reserved
+ * room -- not expected, the room is the bound; the plan is unchanged),
+ * MLA_ERR_HIP (the copy could not be enqueued; destroy the plan).
+ */
+mla_status mla_decode_plan_update(mla_plan* plan, const int32_t* seq_lens_host, void* stream);
 
 /* Same as mla_decode_plan but makes no HIP call at all (num_cus must be > 0):
  * the plan can be inspected with mla_plan_query but not run (mla_decode then
@@ -365,8 +390,9 @@ mla_status mla_o_project(int32_t batch, int32_t q_len, int32_t k_in, int32_t n_o
                          const void* x, const void* w_o, void* y,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Free a plan (its host memory and its device schedule).  NULL is a no-op.
- * The plan must not be in use by a kernel still running. */
+/* Free a plan (its host memory, pinned staging memory and device schedule;
+ * waits for its last schedule upload).  NULL is a no-op.  The plan must not be
+ * in use by a kernel still running. */
 void mla_decode_plan_destroy(mla_plan* plan);
 
 /* Static description of a status code. */

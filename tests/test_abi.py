@@ -144,6 +144,21 @@ def test_decode_refuses_host_only_plan(host_plan):
     assert _call(host_plan, bt_stride=63) == 1  # exactly enough pages is fine up to the plan check
 
 
+def test_plan_update_argument_checks(host_plan):
+    L = mla.lib()
+    lens = np.array([3000, 20], dtype=np.int32)
+    ptr = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.mla_decode_plan_update(None, ptr, None) == 1
+    assert L.mla_decode_plan_update(host_plan.handle, None, None) == 1
+    # a host-only plan has no device schedule to update (refused before any HIP call)
+    assert L.mla_decode_plan_update(host_plan.handle, ptr, None) == 1
+    assert "_plan_host" in L.mla_last_error().decode()
+    with pytest.raises(ValueError):
+        host_plan.update([1, 2, 3])  # wrong batch
+    # the plan is unchanged
+    assert host_plan.query(bnd.MLA_Q_NUM_PARTIALS) > 0
+
+
 def test_plan_query_keys(host_plan):
     assert host_plan.query(bnd.MLA_Q_ROWS_PER_BLOCK) in (64, 128)
     assert host_plan.query(bnd.MLA_Q_TILE_TOKENS) in (32, 64)
