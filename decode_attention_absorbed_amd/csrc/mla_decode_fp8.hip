@@ -573,13 +573,18 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     // QK^T of one tile: acc[kb] = S^T block (keys 32kb.., the wave's 32 rows).
     auto qk_tile = [&](int stage, f32x16(&acc)[2], auto&& extra) {
       const uint32_t base = lds_addr(smem + stage * kStageBytes8);
+      // One address register per operand half for the whole tile; every read
+      // adds a compile-time offset in the instruction (the empty asm keeps
+      // the compiler from splitting the sum into a per-read VALU op).
+      uint32_t b0 = base + qk_off0, b1 = base + qk_off1;
+      asm volatile("" : "+v"(b0), "+v"(b1));
       // MFMA m = 2s + kb; its operand is read one MFMA ahead.
       constexpr int D = kQkDepth8;
       i32x8 a[D + 1];
       auto read = [&](int m, i32x8& dst) {
-        const uint32_t o = base + 18432 * (m & 1) + 2048 * (m >> 1);
-        const f32x4 lo = *LDS_AS(const f32x4, (uintptr_t)(o + qk_off0));
-        const f32x4 hi = *LDS_AS(const f32x4, (uintptr_t)(o + qk_off1));
+        const uint32_t o = 18432 * (m & 1) + 2048 * (m >> 1);
+        const f32x4 lo = *LDS_AS(const f32x4, (uintptr_t)(b0 + o));
+        const f32x4 hi = *LDS_AS(const f32x4, (uintptr_t)(b1 + o));
         dst = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
 #pragma unroll
@@ -596,26 +601,39 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     };
 
     // O^T += V^T P^T for one tile (16 column blocks, 4 transposed reads each).
-    auto read_v = [&](int stage, int cb, i32x8& dst) {
-      const uint32_t base = lds_addr(smem + stage * kStageBytes8) + pv_off0 + 1024 * cb;
-      i32x2 r0 = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)base)));
-      i32x2 r1 = __builtin_bit_cast(
-          i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(base ^ 256u))));
+    // Addresses of the four reads of column block cb: v0 + 1024 cb, v1 +
+    // 1024 cb and both + 18432, with v0 = stage + pv_off0 and v1 = stage +
+    // (pv_off0 ^ 256) (stage bases and 1024 cb leave bits 0..9 alone, so the
+    // bit-8 flip of the other row half commutes with the sum).
+    struct PvBase8 {
+      uint32_t v0, v1;
+    };
+    auto pv_base = [&](int stage) {
+      const uint32_t st = lds_addr(smem + stage * kStageBytes8);
+      PvBase8 pb{st + pv_off0, st + (pv_off0 ^ 256)};
+      asm volatile("" : "+v"(pb.v0), "+v"(pb.v1));  // one register each for the tile
+      return pb;
+    };
+    auto read_v = [&](const PvBase8& pb, int cb, i32x8& dst) {
+      const uint32_t o = 1024 * cb;
+      i32x2 r0 = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(pb.v0 + o))));
+      i32x2 r1 = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(pb.v1 + o))));
       i32x2 r2 = __builtin_bit_cast(
-          i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(base + 18432))));
+          i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(pb.v0 + o + 18432))));
       i32x2 r3 = __builtin_bit_cast(
-          i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)((base ^ 256u) + 18432))));
+          i32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_AS(i32x2, (uintptr_t)(pb.v1 + o + 18432))));
       dst = i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
     };
     const int one_e8m0 = 127;  // V^T is not scaled
     auto pv_tile = [&](int stage, const i32x8& pt, int pscale, auto&& extra) {
       constexpr int DV = kPvDepth8;
+      const PvBase8 pb = pv_base(stage);
       i32x8 v[DV + 1];
 #pragma unroll
-      for (int d = 0; d < DV; ++d) read_v(stage, d, v[d]);
+      for (int d = 0; d < DV; ++d) read_v(pb, d, v[d]);
       static_for<16>([&](auto cbc) {
         constexpr int cb = decltype(cbc)::value;
-        if constexpr (cb + DV < 16) read_v(stage, cb + DV, v[(cb + DV) % (DV + 1)]);
+        if constexpr (cb + DV < 16) read_v(pb, cb + DV, v[(cb + DV) % (DV + 1)]);
         extra(cb);
         OBlock8<cb>::mfma(v[cb % (DV + 1)], pt, one_e8m0, pscale);
         __builtin_amdgcn_sched_barrier(0);
