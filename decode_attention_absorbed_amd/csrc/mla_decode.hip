@@ -546,6 +546,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     float alpha[2] = {1.f, 1.f};
     bool any_scale = false;
     float mx[2], mu[2] = {kMuFloor, kMuFloor};
+    bool ref_check = true;  // some row of the wave may move its reference this tile
     bf16x2 pw[2][4];  // P^T operand under construction: K slots 2m, 2m+1
     float p_even = 0.f;
     float xt[2];  // exponent of the element whose exp comes next
@@ -554,11 +555,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // 4grp + i, row block hb), as kSoftmaxSteps short steps so that it can be
     // spread between MFMAs:
     //   0-3: mask block (kb, hb)'s keys past the row's limit (only on tiles
-    //        that need it), 4: both row blocks' max, 5-8: max over the 4
-    //        lane groups,
-    //   9-10: reference update (a row moves its reference only when its
-    //      maximum grows by more than kRescaleThreshold; the first finite
-    //      maximum needs no rescale because nothing has been accumulated yet),
+    //        that need it), 4: both row blocks' max over this lane's keys and
+    //        whether any lane of the wave passes its row's threshold,
+    //   5: only then (after fewer than one tile in a thousand, measured): max
+    //      over the 4 lane groups and the reference update (a row moves its
+    //      reference only when its maximum grows by more than
+    //      kRescaleThreshold; the first finite maximum needs no rescale
+    //      because nothing has been accumulated yet); 6-10: nothing,
     //   11-27: p = 2^(s * scale - mu), running sum, bf16 pairs of P^T (K slot
     //      j of row block hb is s[2(j/4) + hb][j%4]); software-pipelined so
     //      that a step's exp never waits on the same step's fma.
@@ -573,40 +576,49 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           }
         }
       } else if (step == 4) {
+        bool exceed = false;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const f32x4& x0 = s[hb];
           const f32x4& x1 = s[2 + hb];
           mx[hb] = max3(max3(x0[0], x0[1], x0[2]), max3(x0[3], x1[0], x1[1]), max3(x1[2], x1[3], x1[3]));
+          exceed = exceed || (mx[hb] * scale_log2 > m_ref[hb] + kRescaleThreshold);
         }
-      } else if (step < 9) {
-        const int hb = (step - 5) >> 1;
-        mx[hb] = (step & 1) ? group_max32(mx[hb]) : group_max16(mx[hb]);
+        // A row's reference can only move if the maximum of one of its
+        // lanes' keys passes it by the threshold (the row maximum is one of
+        // them, and rounding the product is monotonic); otherwise steps 5-10
+        // would leave every reference and sum as it is (alpha = 2^0), so the
+        // wave skips them.
+        ref_check = __builtin_amdgcn_ballot_w64(exceed) != 0;
       } else if (step < 11) {
-        {
+        if (step == 5 && ref_check) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) mx[hb] = group_max16(group_max32(mx[hb]));
           // mu = max(m_ref, kMuFloor) is the reference actually subtracted,
           // so alpha = 2^(mu_old - mu_new) needs no case for -inf: it is 1
           // without an update and 0 for a row's first finite maximum (when
           // nothing has been accumulated for that row).
-          const int hb = step - 9;
-          const float m = mx[hb] * scale_log2;
-          const bool upd = m > m_ref[hb] + kRescaleThreshold;
-          const float m_new = upd ? (POW2 ? __builtin_ceilf(m) : m) : m_ref[hb];
-          const float mu_new = fmaxf(m_new, kMuFloor);
-          if constexpr (POW2) {
-            // alpha holds the integer exponent mu - mu_new <= 0 (clamped:
-            // a first finite maximum scales a sum that is still 0).
-            alpha[hb] = fmaxf(mu[hb] - mu_new, -256.f);
-            l_part[hb] = __builtin_ldexpf(l_part[hb], (int)alpha[hb]);
-            l_wt[hb] = __builtin_ldexpf(l_wt[hb], (int)alpha[hb]);
-          } else {
-            alpha[hb] = __builtin_amdgcn_exp2f(mu[hb] - mu_new);
-            l_part[hb] *= alpha[hb];
-            l_wt[hb] *= alpha[hb];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const float m = mx[hb] * scale_log2;
+            const bool upd = m > m_ref[hb] + kRescaleThreshold;
+            const float m_new = upd ? (POW2 ? __builtin_ceilf(m) : m) : m_ref[hb];
+            const float mu_new = fmaxf(m_new, kMuFloor);
+            if constexpr (POW2) {
+              // alpha holds the integer exponent mu - mu_new <= 0 (clamped:
+              // a first finite maximum scales a sum that is still 0).
+              alpha[hb] = fmaxf(mu[hb] - mu_new, -256.f);
+              l_part[hb] = __builtin_ldexpf(l_part[hb], (int)alpha[hb]);
+              l_wt[hb] = __builtin_ldexpf(l_wt[hb], (int)alpha[hb]);
+            } else {
+              alpha[hb] = __builtin_amdgcn_exp2f(mu[hb] - mu_new);
+              l_part[hb] *= alpha[hb];
+              l_wt[hb] *= alpha[hb];
+            }
+            any_scale = any_scale || (upd && mu[hb] > kMuFloor);
+            m_ref[hb] = m_new;
+            mu[hb] = mu_new;
           }
-          any_scale = any_scale || (upd && mu[hb] > kMuFloor);
-          m_ref[hb] = m_new;
-          mu[hb] = mu_new;
         }
       } else if (step < kSoftmaxSteps) {
         const int j = step - 11;  // 0..16: exp of element j-1, fma of element j
