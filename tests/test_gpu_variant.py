@@ -127,3 +127,25 @@ def test_unknown_variant_is_refused(dev):
     with pytest.raises(mla.MLAError, match="variant"):
         mla.mla_decode_variant(plan, t["q_nope"], t["q_pe"], t["cache"], t["block_table"], t["seq_lens"],
                                x.softmax_scale, variant=2)
+
+
+@pytest.mark.parametrize("num_cus", [7, 64, 256])
+def test_pow2_splits_agree_to_the_partials_rounding(dev, num_cus):
+    """With a power-of-two reference, a piece's weights are exact power-of-two
+    multiples of the unsplit run's, so their bf16 rounding is the same: split
+    and unsplit runs differ only by the fp16 storage of the partials (at most
+    2^-11 of the largest |V| of the request, per element) and fp32 summation
+    order.  The lazy form rounds P against each piece's own maximum, so it
+    agrees only to the bf16 level (printed for comparison)."""
+    x = make_inputs(3, 128, 2, 64, [3000, 1500, 700], seed=57)
+    vmax = float(np.max(np.abs(x.cache_f64()[:, :, :512])))
+    bound = 2.0**-11 * vmax + 1e-6
+    diffs = {}
+    for name in ("pow2", "lazy"):
+        o1, l1, _ = run_variant(x, dev, VARIANTS[name], num_cus=1)
+        o2, l2, _ = run_variant(x, dev, VARIANTS[name], num_cus=num_cus)
+        diffs[name] = (float(np.max(np.abs(o2 - o1))), float(np.max(np.abs(l2 - l1))))
+    print(f"num_cus={num_cus}: split vs whole max|d out| pow2 {diffs['pow2'][0]:.2e}, lazy {diffs['lazy'][0]:.2e}"
+          f" (bound {bound:.2e}); max|d lse| pow2 {diffs['pow2'][1]:.2e}", flush=True)
+    assert diffs["pow2"][0] <= bound
+    assert diffs["pow2"][1] <= 1e-5
