@@ -29,6 +29,8 @@ namespace mla {
 namespace {
 
 constexpr int kOk = 0, kInvalid = 1, kUnsupported = 2;
+// Largest CU count a plan is made for (bounds the schedule's size; MI355X has 256).
+constexpr int32_t kMaxCus = 65536;
 
 struct Piece {
   int32_t b, t0, t1;  // tile range
@@ -102,8 +104,8 @@ int build_plan(const int32_t* lens, int32_t batch, int32_t q_len, int32_t heads,
     *err = "page_size must be a power of two in [16, 4096]";
     return kUnsupported;
   }
-  if (num_cus <= 0) {
-    *err = "num_cus must be >= 1";
+  if (num_cus <= 0 || num_cus > kMaxCus) {
+    *err = "num_cus must be in [1, 65536]";
     return kInvalid;
   }
   for (int32_t b = 0; b < batch; ++b) {

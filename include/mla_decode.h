@@ -71,7 +71,8 @@ typedef struct mla_plan mla_plan;
  *                 token; query j sees one key more than query j-1).
  *  num_heads      1 <= num_heads <= 128, and q_len * num_heads <= 1024.
  *  page_size      tokens per cache page: a power of two, 16 <= page_size <= 4096.
- *  num_cus        compute units to plan for; 0 = ask the current device.
+ *  num_cus        compute units to plan for, at most 65536; 0 = ask the
+ *                 current device.
  *  plan_out       receives the new plan (set to NULL on failure).
  *
  * Allocates host memory, pinned host memory and a small device buffer holding

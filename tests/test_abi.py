@@ -54,6 +54,8 @@ def test_status_strings():
         (dict(seq_lens=[5, 0], q_len=1, num_heads=16, page_size=16, num_cus=8), 1),
         (dict(seq_lens=[(1 << 24) + 1], q_len=1, num_heads=16, page_size=16, num_cus=8), 2),
         (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=16, num_cus=0), 1),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=16, num_cus=65536), 0),
+        (dict(seq_lens=[5], q_len=1, num_heads=16, page_size=16, num_cus=65537), 1),
     ],
 )
 def test_plan_argument_checks(args, status):
