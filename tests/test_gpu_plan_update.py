@@ -1,7 +1,8 @@
 """mla_decode_plan_update on an MI355X: a plan re-planned in place for new
 lengths (same batch shape) gives exactly what a fresh plan gives, updates
 are ordered on the stream (decodes enqueued before an update keep the old
-schedule), and a refused update leaves the plan as it was."""
+schedule), and a refused update leaves the plan as it was; the same for the
+FP8 kernel's plans."""
 import numpy as np
 import pytest
 
@@ -73,4 +74,36 @@ def test_refused_update_leaves_the_plan_unchanged(dev):
     o2, l2 = decode(x, t, plan)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    plan.destroy()
+
+
+def test_fp8_plan_update_matches_fresh_plans(dev):
+    """The FP8 kernel's plans (64-key tiles) are re-planned the same way."""
+    from workloads import make_inputs_fp8
+
+    H, q, P = 128, 2, 64
+    xs = [make_inputs_fp8(3, H, q, P, lens, seed=s) for lens, s in (([3000, 700, 65], 65), ([90, 5000, 1200], 66),
+                                                                      ([2, 2, 8000], 67))]
+    ts = [x.to_torch(dev) for x in xs]
+
+    def run(x, t, plan):
+        return mla.binding.mla_decode_fp8(plan, t["q_nope"], t["q_pe"], t["cache_codes"], t["cache_exps"],
+                                          t["block_table"], t["seq_lens"], x.softmax_scale)
+
+    refs = []
+    for x, t in zip(xs, ts):
+        fresh = mla.binding.mla_decode_fp8_plan(x.seq_lens, q, H, P, 0)
+        o, l = run(x, t, fresh)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), l.clone()))
+        fresh.destroy()
+    plan = mla.binding.mla_decode_fp8_plan(xs[0].seq_lens, q, H, P, 0)
+    outs = []
+    for i in (0, 1, 2, 0):
+        if outs:
+            plan.update(xs[i].seq_lens)
+        outs.append((i,) + run(xs[i], ts[i], plan))
+    torch.cuda.synchronize()
+    for i, o, l in outs:
+        assert torch.equal(o, refs[i][0]) and torch.equal(l, refs[i][1]), i
     plan.destroy()
