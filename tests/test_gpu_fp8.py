@@ -135,6 +135,21 @@ def test_fp8_forced_split_counts(dev, num_cus):
     compare(out, lse, *oracle(x), what=f"num_cus={num_cus}")
 
 
+@pytest.mark.parametrize("q_len,page", [(1, 16), (2, 64)])
+def test_fp8_many_short_requests(dev, q_len, page):
+    """60 requests of 1..300 keys (16 heads, to keep the oracle's query
+    quantization short) planned for 8 CUs: every workgroup runs several
+    requests one after another, every request against the oracle."""
+    rng = np.random.default_rng(7 + q_len)
+    lens = rng.integers(q_len, 301, size=60).tolist()
+    x = make_inputs_fp8(len(lens), 16, q_len, page, lens, seed=310 + q_len)
+    plan = bnd.mla_decode_fp8_plan(x.seq_lens, x.q_len, x.heads, x.page, 8)
+    wg = plan.workgroups()
+    assert (wg[:, 1] - wg[:, 0]).min() >= 3
+    out, lse = run_gpu(x, dev, plan=plan)
+    compare(out, lse, *oracle(x), what=f"60 short requests, q_len {q_len}, page {page}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp", "mixed", "long", "mtp4", "mtp8"])
 def test_fp8_named_workload_parity(dev, name):
     x = make_config_fp8(name)

@@ -239,3 +239,21 @@ def test_long_draft_workloads(dev, name):
     out, lse = run_gpu(x, dev)
     ref_o, ref_l = oracle(x)
     compare(out, lse, ref_o, ref_l, what=f"{name}, all {x.batch} requests")
+
+
+# ---- many short requests: several pieces per workgroup ------------------------------------
+
+
+@pytest.mark.parametrize("q_len,page", [(1, 16), (2, 64)])
+def test_many_short_requests(dev, q_len, page):
+    """400 requests of 1..300 keys planned for 64 CUs: every workgroup runs
+    several requests one after another (query reload, stage reuse and the
+    barrier between pieces), every request against the oracle."""
+    rng = np.random.default_rng(7 + q_len)
+    lens = rng.integers(q_len, 301, size=400).tolist()
+    x = make_inputs(len(lens), 128, q_len, page, lens, seed=300 + q_len)
+    plan = mla.mla_decode_plan(x.seq_lens, x.q_len, x.heads, x.page, 64)
+    wg = plan.workgroups()
+    assert (wg[:, 1] - wg[:, 0]).min() >= 3  # several pieces per workgroup
+    out, lse = run_gpu(x, dev, plan=plan)
+    compare(out, lse, *oracle(x), what=f"400 short requests, q_len {q_len}, page {page}")
