@@ -152,7 +152,9 @@ size_t mla_decode_workspace_bytes(const mla_plan* plan);
  *                   Contents on entry are ignored; it is scratch for this call.
  *  stream           hipStream_t to enqueue on; NULL = the default stream.
  *
- * Enqueues at most two kernels, allocates nothing, never synchronizes.  The
+ * Enqueues at most two kernels and nothing else (no memset, no copy), allocates
+ * nothing, never synchronizes, so a call may be captured in a HIP graph and
+ * replayed (the graph then holds the plan's and buffers' addresses).  The
  * result is deterministic for a given plan.  Argument checks run on the host
  * before any HIP call.  Errors: MLA_ERR_INVALID_ARGUMENT,
  * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP (launch failure).
