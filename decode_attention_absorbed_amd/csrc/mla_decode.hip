@@ -351,7 +351,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) lim[hb] = row_ok[hb] ? min(kv1, L - q_len + 1 + jq[hb]) : kv0;
     // A tile starting at key tb needs masking iff tb + kTile > lim_wave.
-    const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
+    // uniform: the per-tile masking test is then a scalar compare and branch
+    const int lim_wave = __builtin_amdgcn_readfirstlane(wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0);
 
     // Block-table entries of a tile (checked when used).
     auto page_at = [&](int pidx) {
@@ -565,15 +566,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     //   11-27: p = 2^(s * scale - mu), running sum, bf16 pairs of P^T (K slot
     //      j of row block hb is s[2(j/4) + hb][j%4]); software-pipelined so
     //      that a step's exp never waits on the same step's fma.
-    auto softmax_step = [&](int step, f32x4(&s)[4], bool need_mask, int tb_s) {
+    auto softmax_step = [&](int step, f32x4(&s)[4], int need_mask, int tb_s) {
       if (step < 4) {
         const int kbk = step >> 1, hb = step & 1;
-        if (__builtin_amdgcn_readfirstlane((int)need_mask)) {  // uniform: branch, not an exec mask
+        if (need_mask) {  // uniform (scalar compare of uniform limits): a scalar branch
+          // Keys left of the row's limit: lim - (this lane's first key), so
+          // that the per-key test is one compare against a constant; the
+          // empty asm keeps the subtraction inside the branch.
+          int room = lim[hb] - (tb_s + 16 * kbk + 4 * grp);
+          asm volatile("" : "+v"(room));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = tb_s + 16 * kbk + 4 * grp + i;
-            s[2 * kbk + hb][i] = tok < lim[hb] ? s[2 * kbk + hb][i] : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) s[2 * kbk + hb][i] = i < room ? s[2 * kbk + hb][i] : -INFINITY;
         }
       } else if (step == 4) {
         bool exceed = false;
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     {
       f32x4 s0[4];
       qk_tile(smem, s0, [](int) {}, [](int) {}, true);
-      const bool nm0 = kv0 + kTile > lim_wave;
+      const int nm0 = kv0 + kTile > lim_wave ? 1 : 0;  // uniform (scalar)
 #pragma unroll
       for (int step = 0; step < kSoftmaxSteps; ++step) softmax_step(step, s0, nm0, kv0);
       pack_p(pb);
@@ -734,7 +737,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
       // ---- PV of tile it, softmax of tile it+1 between its MFMAs (from
       //      column block 4 on: by then the QK^T results are readable) ----
       if (has_next) {
-        const bool nm = tb + 2 * kTile > lim_wave;
+        const int nm = tb + 2 * kTile > lim_wave ? 1 : 0;  // uniform (scalar)
         pv_run(vb, pb, v, [&](int cb) {
           if (cb < kLoadsPerWave - 5) {
             copy_at(5 + cb);

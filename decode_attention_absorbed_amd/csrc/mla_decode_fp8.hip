@@ -397,7 +397,8 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
     const int L = seq_lens[b];
     const bool bad_len = (L != planned_lens[b]);
     const int lim = row_ok ? min(kv1, L - q_len + 1 + jq) : kv0;
-    const int lim_wave = wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0;
+    // uniform: the per-tile masking test is then a scalar compare and branch
+    const int lim_wave = __builtin_amdgcn_readfirstlane(wave_full ? min(kv1, L - q_len + 1 + wave_jq0) : kv0);
 
     auto page_at = [&](int pidx) {
       const int rel = pidx - first_pg;
@@ -680,15 +681,19 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
         pt[4 * kb + a] = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * sc[0], p1 * sc[1], 0, false);
       if (h == 1 && q + 2 < 8) sc_read(q + 2);
     };
-    auto softmax_step = [&](int step, f32x16(&s)[2], bool need_mask, int tb_s, i32x8& pt, int& pscale) {
+    auto softmax_step = [&](int step, f32x16(&s)[2], int need_mask, int tb_s, i32x8& pt, int& pscale) {
       if (step == 0) {
-        if (__builtin_amdgcn_readfirstlane((int)need_mask)) {
+        if (need_mask) {  // uniform (scalar compare of uniform limits): a scalar branch
+          // Keys left of the row's limit, counted from this lane's first key;
+          // the empty asm keeps the subtraction inside the branch.
+          int room = lim - (tb_s + 4 * g);
+          asm volatile("" : "+v"(room));
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int tok = tb_s + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-              s[kb][r] = tok < lim ? s[kb][r] : -INFINITY;
+              const int k = 32 * kb + 8 * (r >> 2) + (r & 3);
+              s[kb][r] = k < room ? s[kb][r] : -INFINITY;
             }
         }
         float m0 = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[0][4], s[0][5]), max3(s[0][6], s[0][7], s[0][8]));
@@ -737,7 +742,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       f32x16 s0[2];
       prep_scales(0, kv0);
       qk_tile(0, s0, [](int) {});
-      const bool nm0 = kv0 + kTile8 > lim_wave;
+      const int nm0 = kv0 + kTile8 > lim_wave ? 1 : 0;  // uniform (scalar)
 #pragma unroll
       for (int step = 0; step < kSmSteps8; ++step) softmax_step(step, s0, nm0, kv0, pt, psc);
       any_scale = false;  // nothing accumulated yet
@@ -778,7 +783,7 @@ __global__ __launch_bounds__(64 * kWaves8, 1) void decode_fp8_kernel(
       __builtin_amdgcn_sched_barrier(0);
 
       if (has_next) {
-        const bool nm = tb + 2 * kTile8 > lim_wave;
+        const int nm = tb + 2 * kTile8 > lim_wave ? 1 : 0;  // uniform (scalar)
         pv_tile(st_cur, pt, psc, [&](int cb) {
           softmax_step(cb, s_next, nm, tb + kTile8, pt_next, psc_next);
         });
