@@ -280,3 +280,11 @@ def test_fp8_scale_reference_moves(dev):
         x.cache_exps[pg, sl] = (x.cache_exps[pg, sl].astype(np.int32) - 70).astype(np.uint8)
     out, lse = run_gpu(x, dev, num_cus=1)
     compare(out, lse, *oracle(x), what="scale reference moves")
+
+
+def test_fp8_one_million_key_request(dev):
+    """One request of 1,048,576 keys (0.6 GB of codes, page 4096) split over
+    the whole device, every row against the oracle."""
+    x = make_inputs_fp8(1, 128, 1, 4096, [1 << 20], seed=402)
+    out, lse = run_gpu(x, dev)
+    compare(out, lse, *oracle(x), what="2^20 keys, page 4096")

@@ -257,3 +257,18 @@ def test_many_short_requests(dev, q_len, page):
     assert (wg[:, 1] - wg[:, 0]).min() >= 3  # several pieces per workgroup
     out, lse = run_gpu(x, dev, plan=plan)
     compare(out, lse, *oracle(x), what=f"400 short requests, q_len {q_len}, page {page}")
+
+
+# ---- one request of 2^20 keys ---------------------------------------------------------------
+
+
+@pytest.mark.parametrize("page", [16, 4096])
+def test_one_million_key_request(dev, page):
+    """One request of 1,048,576 keys (1.2 GB of cache) split over the whole
+    device: pieces of 128 tiles, 256 partials merged by the combine, page ids
+    up to 65535 (page 16: 256 pages per piece, nearly all looked up past the
+    first 64), every row against the oracle."""
+    x = make_inputs(1, 128, 1, page, [1 << 20], seed=401)
+    print(f"page {page}: {x.num_pages} pages", flush=True)
+    out, lse = run_gpu(x, dev)
+    compare(out, lse, *oracle(x), what=f"2^20 keys, page {page}")
