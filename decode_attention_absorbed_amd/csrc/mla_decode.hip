@@ -75,7 +75,6 @@ constexpr int kLoadsPerTile = kTile * kChunks / 64;     // 36 one-KB copies
 constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;  // 9
 constexpr int kQSteps = 576 / 32;                      // 18 K steps of QK^T
 constexpr int kNopeSteps = 512 / 32;                   // the first 16 come from c_kv
-constexpr int kQpeWaveBytes = 32 * 64 * 2;             // q_pe of one wave's 32 rows in LDS
 #ifndef MLA_QK_DEPTH
 #define MLA_QK_DEPTH 1
 #endif
@@ -247,10 +246,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     float scale_log2, int32_t rows, int32_t heads, int32_t q_len, int32_t page_log2, int32_t nrb,
     float* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
     float* __restrict__ ws_lse, float* __restrict__ ws_f, uint32_t* __restrict__ rescale_events) {
-  // 4 tile stages (144 KB) + the rope part of the query rows (16 KB): the
-  // 160 KB of LDS a workgroup may hold.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kWaves * kQpeWaveBytes];
-  uint8_t* const qpe_lds = smem + kStages * kStageBytes;
+  // 4 tile stages (144 KB); the query rows live in registers.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const WorkgroupRange wr = wgs[blockIdx.x];
   if (wr.seg_begin >= wr.seg_end) return;
@@ -297,12 +294,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
   // reads key row dma_row, bytes dma_col + 128 i of it.
   const int dma_row = (lane & 31) ^ (16 * (lane >> 5));
   const int dma_col = 16 * (lane >> 5) + 32 * wave;
-  // Rope part of the query (dims 512..575) in LDS: row r (0..31) of wave w
-  // at w * 4096 + 128 r, its 16-byte chunk c at slot c ^ ((r >> 1) & 7), so
-  // that a half wave (16 rows, chunks 4e and 4e + 1) hits distinct banks.
-  // B operand of step 16 + e, row block hb: row 16hb + l16, chunk 4e + grp;
-  // e = 1 is e = 0 with address bit 6 flipped.
-  const uint32_t qpe_base = lds_addr(qpe_lds) + wave * kQpeWaveBytes + l16 * 128 + 16 * (grp ^ ((l16 >> 1) & 7));
 
   for (int si = wr.seg_begin; si < wr.seg_end; ++si) {
     const Segment sg = segs[si];
@@ -320,27 +311,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     const int last_pg = (kv1 - 1) >> page_log2;
     int pg_lane = load4(bt_row + min(first_pg + lane, last_pg));
 
-    // Query rows as the B operand: q[16hb + ks] holds dims 32ks + 8grp .. +7
-    // of row hb (c_kv part, registers); the rope part is copied to this
-    // wave's LDS slice (4 copies of 1 KB: slot p = row p/8, chunk p%8).  Rows
+    // Query rows as the B operand, all in registers: q[16hb + ks] holds
+    // dims 32ks + 8grp .. +7 of row hb (the c_kv part, steps 0..15) and
+    // qr[e][hb] dims 32e + 8grp .. +7 of its rope part (steps 16 + e).  Rows
     // past the end load row 0: their scores are masked and they are never
-    // stored.  Only this wave reads its slice, so the copies need no barrier.
+    // stored.
     bf16x8 q[2 * kNopeSteps];
+    bf16x8 qr[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int qrow = row_ok[hb] ? row[hb] : 0;
       const uint16_t* qn = q_nope + ((int64_t)b * rows + qrow) * 512 + 8 * grp;
+      const uint16_t* qp = q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < kNopeSteps; ++ks) q[kNopeSteps * hb + ks] = load16(qn + 32 * ks);
-    }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int pidx = n * 64 + lane;
-      const int r = pidx >> 3;
-      const int c = (pidx & 7) ^ ((r >> 1) & 7);
-      const int qr = wave_row0 + r;
-      const int qrow = qr < rows ? qr : 0;
-      dma16(q_pe + ((int64_t)b * rows + qrow) * 64 + 8 * c, lds_addr(qpe_lds + wave * kQpeWaveBytes + n * 1024));
+      for (int e = 0; e < 2; ++e) qr[e][hb] = load16(qp + 32 * e);
     }
 
     const int L = seq_lens[b];
@@ -429,8 +415,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     // tiles of this one land in LDS.
     __syncthreads();
 
-    // Page ids have landed once only the 36 query copies are in flight.
-    wait_vmem<2 * kNopeSteps + 4>();
+    // Page ids have landed once only the 36 query loads are in flight.
+    wait_vmem<2 * kNopeSteps + 4>();  // 32 c_kv + 4 rope
     asm volatile("" : "+v"(pg_lane));
 
     const int last_tile = ntiles - 1;
@@ -467,20 +453,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
     auto qk_tile = [&](const uint8_t* kb, f32x4(&acc)[4], auto&& extra, auto&& tail, bool drain) {
       constexpr int D = kQkDepth;
       bf16x8 a[D + 1][2];
-      bf16x8 qb[2][2];  // rope steps: [e][hb]
       // Stage bases are multiples of 512 bytes: bit 8 of the sum is the lane's.
       const uint32_t k0 = lds_addr(kb) + qk_off0, k1 = k0 ^ 256u;
       // Read of step ks issued in slot j: key block 0 (j = 0), key block 1
-      // (j = 2), and on rope steps the query's rope chunks (j = 1, 3).
+      // (j = 2); slots 1 and 3 issue none.
       auto read = [&](int ks, int j) {
         if (j == 0) {
           a[ks % (D + 1)][0] = *LDS_AS(const bf16x8, (uintptr_t)(k0 + 2048 * ks));
         } else if (j == 2) {
           a[ks % (D + 1)][1] = *LDS_AS(const bf16x8, (uintptr_t)(k1 + 2048 * ks));
-        } else if (ks >= kNopeSteps) {
-          const int e = ks - kNopeSteps, hb = j >> 1;
-          const uint32_t qa = e ? qpe_base ^ 64u : qpe_base;
-          qb[e][hb] = *LDS_AS(const bf16x8, (uintptr_t)(qa + 2048 * hb));
         }
       };
 #pragma unroll
@@ -495,7 +476,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
           if (ks + D < kQSteps) read(ks + D, j);
           if (ks == kQSteps - 1) tail(j);
           extra(4 * ks + j);
-          const bf16x8& bq = ks < kNopeSteps ? q[kNopeSteps * (j & 1) + ks] : qb[ks - kNopeSteps][j & 1];
+          const bf16x8& bq = ks < kNopeSteps ? q[kNopeSteps * (j & 1) + ks] : qr[ks - kNopeSteps][j & 1];
           s_mfma(acc[j], a[ks % (D + 1)][j >> 1], bq, ks == 0);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -672,6 +653,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_kernel(
                    "+v"(q[22]), "+v"(q[23]));
       asm volatile("" : "+v"(q[24]), "+v"(q[25]), "+v"(q[26]), "+v"(q[27]), "+v"(q[28]), "+v"(q[29]),
                    "+v"(q[30]), "+v"(q[31]));
+      asm volatile("" : "+v"(qr[0][0]), "+v"(qr[0][1]), "+v"(qr[1][0]), "+v"(qr[1][1]));
       __syncthreads();
     }
     o_zero_rec<0>();

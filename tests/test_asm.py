@@ -50,12 +50,13 @@ def test_no_mfma_result_to_valu_hazards(asm):
 
 def test_async_query_loads_untouched_until_waited(asm):
     for body in asm_checks.kernel_bodies(asm):
-        assert sum(t.startswith("global_load_dwordx4") for t in body) == 32
+        # the query rows: 32 c_kv chunks and 4 rope chunks per lane
+        assert sum(t.startswith("global_load_dwordx4") for t in body) == 36
         assert asm_checks.async_load_violations(body) == []
 
 
 def test_only_explicit_vmcnt_waits(asm):
-    # 36 = query copies in flight (page ids landed), 18 = two tiles of copies
+    # 36 = query loads in flight (page ids landed), 18 = two tiles of copies
     # in flight (prologue), 9 = one tile (loop), 0 = drain
     for body in asm_checks.kernel_bodies(asm):
         waits = asm_checks.vmcnt_waits(body)
