@@ -28,7 +28,8 @@ rotate over copies larger than the last-level cache, as each layer has its own).
 HBM traffic evidence (roofline.traffic): rocprofv3 counter passes over this
 script, one counter per pass, for the decode workload and for a plain device
 copy of known size (--calibrate-copy), turned into profiles/traffic_<config>.json
-by --traffic-from; the commands are listed in profiles/traffic_<config>.md.
+by --traffic-from; the commands are listed in the profile summaries under
+profiles/ (decode_<workload>_profile.md, decode_fp8_traffic_profile.md).
 """
 from __future__ import annotations
 
