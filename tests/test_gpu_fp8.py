@@ -257,6 +257,25 @@ def _pages_of(x, b, t0, t1):
     return x.block_table[b, t // x.page], t % x.page
 
 
+@pytest.mark.parametrize("part", ["rope", "c_kv"])
+def test_fp8_one_query_part_alone_decides_the_scores(dev, part):
+    # As for the bf16 cache: the other part of every query row is zero (its
+    # MXFP8 blocks quantize to zero codes), so the scores come from the rope
+    # dimensions alone (the rope part scaled by 4, exact in bf16) or from
+    # the c_kv dimensions alone.
+    for heads, lens, seed in ((128, [300, 97, 33], 23), (16, [260, 5], 24)):
+        x = make_inputs_fp8(len(lens), heads, 2, 64, lens, seed=seed)
+        if part == "rope":
+            x.q_nope[:] = 0
+            pe = x.q_pe.astype(np.uint32)
+            nz = (pe & 0x7F80) != 0  # normal numbers: add 2 to the exponent
+            x.q_pe = np.where(nz, pe + (2 << 7), pe).astype(np.uint16)
+        else:
+            x.q_pe[:] = 0
+        out, lse = run_gpu(x, dev)
+        compare(out, lse, *oracle(x), what=f"{part} part alone, {heads} heads")
+
+
 def test_fp8_row_reference_moves_and_output_rescales(dev):
     # Keys from 256 on get 8x larger scale bytes' worth (+3): their scores
     # dwarf the first tiles' by far more than 2^32 in log2 units, so every

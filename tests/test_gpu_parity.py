@@ -163,6 +163,26 @@ def test_mtp_queries_match_single_query_runs(dev):
     assert np.max(np.abs(o[:, 1] - o1[:, 0])) < 1e-4 and np.max(np.abs(l[:, 1] - l1[:, 0])) < 1e-4
 
 
+@pytest.mark.parametrize("part", ["rope", "c_kv"])
+def test_one_query_part_alone_decides_the_scores(dev, part):
+    # The other part of every query row is zero, so the scores come from the
+    # rope dimensions (512..575) alone, or from the c_kv dimensions alone;
+    # the query's rope part is scaled by 4 (exact in bf16) so that its
+    # scores spread as widely as the c_kv part's.  Rows of both row blocks
+    # of every wave, 16- and 128-head requests, ragged tiles, two query tokens.
+    for heads, lens, seed in ((128, [300, 97, 33], 21), (16, [260, 5], 22)):
+        x = make_inputs(len(lens), heads, 2, 64, lens, seed=seed)
+        if part == "rope":
+            x.q_nope[:] = 0
+            pe = x.q_pe.astype(np.uint32)
+            nz = (pe & 0x7F80) != 0  # normal numbers: add 2 to the exponent
+            x.q_pe = np.where(nz, pe + (2 << 7), pe).astype(np.uint16)
+        else:
+            x.q_pe[:] = 0
+        out, lse = run_gpu(x, dev)
+        compare(out, lse, *oracle(x), what=f"{part} part alone, {heads} heads")
+
+
 def test_repeat_runs_are_bitwise_identical(dev):
     x = make_inputs(4, 128, 1, 64, [2000, 5, 640, 999], seed=13)
     t = x.to_torch(dev)
